@@ -1,0 +1,398 @@
+"""Checks that tie the CPU oracle to facts outside itself.
+
+Each pin takes the oracle module as its argument so that the same checks can
+be run against copies of the oracle with a planted mistake (see
+test_oracle_mutants.py): every plausible slip must fail at least one pin.
+
+Pins come from: values the pages print (tests/golden/*.json), brute force
+written from the definitions with plain Python loops, closed forms, library
+routines (torch's scaled_dot_product_attention, numpy integer matmul) for
+special cases, and invariants of a top-k.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _tiny_inputs(rng, *, n_q, q_pos0, ratio, H, D, Hi, Di, value_range=8):
+    n_raw = q_pos0 + n_q
+    n_comp = n_raw // ratio
+    kv_raw = rng.standard_normal((n_raw, D)).astype(np.float16)
+    groups = kv_raw[: n_comp * ratio].astype(np.float64).reshape(n_comp, ratio, D)
+    kv_comp = (groups.mean(axis=1)).astype(np.float16)
+    return {
+        "q": rng.standard_normal((n_q, H, D)).astype(np.float16),
+        "kv_raw": kv_raw,
+        "kv_comp": kv_comp,
+        "iq": rng.integers(-value_range, value_range, (n_q, Hi, Di)).astype(np.int8),
+        "ik": rng.integers(-value_range, value_range, (n_comp, Di)).astype(np.int8),
+        "iw": rng.integers(1, 5, (n_q, Hi)).astype(np.int8),
+    }
+
+
+# ------------------------------------------------------------ visibility pins
+def pin_visibility_brute_force(orc):
+    """Explicit mask from the definition of a compressed row == analytic form.
+
+    A compressed row j stands for raw rows ratio*j .. ratio*j+ratio-1; it
+    exists once all of them exist and is visible to query t once all of them
+    are at or before t (the explicit-mask versus analytic-mask check named on
+    "perf(ds4): extend sparse prefill scheduling to 10K", Qualification).
+    """
+    for ratio in (1, 2, 3, 4, 5):
+        for n_raw in range(0, 41):
+            groups = []
+            j = 0
+            while True:
+                members = [ratio * j + m for m in range(ratio)]
+                if not all(x < n_raw for x in members):
+                    break
+                groups.append(members)
+                j += 1
+            assert orc.n_compressed(n_raw, ratio) == len(groups), (ratio, n_raw)
+            for t in range(n_raw):
+                explicit = [all(x <= t for x in g) for g in groups]
+                nv = orc.n_visible(t, len(groups), ratio)
+                assert explicit == [True] * nv + [False] * (len(groups) - nv), (ratio, n_raw, t)
+
+
+def pin_window_brute_force(orc):
+    """Window = the W most recent raw rows up to and including t."""
+    for W in (1, 2, 3, 7, 64):
+        for t in range(0, 80):
+            rows = [s for s in range(t + 1) if t - s < W]
+            lo, hi = orc.window_range(t, W)
+            assert list(range(lo, hi)) == rows, (W, t)
+
+
+def pin_mask_memory(orc):
+    """The printed GiB of removed fp32 masks match T x (T + floor(T/4)) keys."""
+    g = _golden("mask_memory.json")
+    for case in g["cases"]:
+        T = case["tokens"]
+        keys = T + orc.n_compressed(T, g["ratio"])
+        gib = g["layers"] * T * keys * 4 / 2**30
+        assert abs(gib - case["gib_printed"]) <= 0.0005 + 1e-12, (T, gib)
+
+
+# --------------------------------------------------------------- indexer pins
+def _indexer_brute(iq, iw, ik, q_pos0, ratio):
+    T, Hi, Di = iq.shape
+    Nc = ik.shape[0]
+    out = [[None] * Nc for _ in range(T)]
+    for r in range(T):
+        t = q_pos0 + r
+        for j in range(Nc):
+            if not all(ratio * j + m <= t for m in range(ratio)):
+                out[r][j] = -(2**31)
+                continue
+            total = 0
+            for h in range(Hi):
+                dot = 0
+                for d in range(Di):
+                    dot += int(iq[r, h, d]) * int(ik[j, d])
+                total += int(iw[r, h]) * (dot if dot > 0 else 0)
+            out[r][j] = total
+    return np.array(out, dtype=np.int64)
+
+
+def pin_indexer_brute_force(orc):
+    rng = np.random.default_rng(11)
+    for (n_q, q_pos0, Hi, Di, ratio) in ((9, 0, 4, 64, 4), (7, 13, 3, 8, 4), (6, 5, 2, 5, 2)):
+        inp = _tiny_inputs(rng, n_q=n_q, q_pos0=q_pos0, ratio=ratio, H=1, D=4, Hi=Hi, Di=Di)
+        got = orc.indexer_scores(inp["iq"], inp["iw"], inp["ik"], q_pos0, ratio)
+        want = _indexer_brute(inp["iq"], inp["iw"], inp["ik"], q_pos0, ratio)
+        assert got.dtype == np.int32
+        np.testing.assert_array_equal(got.astype(np.int64), want)
+
+
+def pin_indexer_closed_forms(orc):
+    """Special cases with a known answer.
+
+    * all inputs >= 0: the ReLU never clips, so S = (sum_h w_h q_h) . k, an
+      integer matmul;
+    * q >= 0, k <= 0: every head dot is <= 0, so every visible score is 0;
+    * weights that select one head: S = ReLU(q_h . k) for that head;
+    * the extreme q = k = -8, w = 4 over 4 x 64 gives 4*4*64*64 = 65536.
+    """
+    rng = np.random.default_rng(12)
+    T, Hi, Di, Nc, ratio, p0 = 12, 4, 64, 20, 4, 70
+    iq = rng.integers(0, 8, (T, Hi, Di)).astype(np.int8)
+    ik = rng.integers(0, 8, (Nc, Di)).astype(np.int8)
+    iw = rng.integers(1, 5, (T, Hi)).astype(np.int8)
+    got = orc.indexer_scores(iq, iw, ik, p0, ratio).astype(np.int64)
+    comb = np.einsum("th,thd->td", iw.astype(np.int64), iq.astype(np.int64))
+    want = comb @ ik.astype(np.int64).T
+    for r in range(T):
+        nv = min(Nc, (p0 + r + 1) // ratio)
+        np.testing.assert_array_equal(got[r, :nv], want[r, :nv])
+        assert (got[r, nv:] == -(2**31)).all()
+
+    neg_k = (-ik).astype(np.int8)
+    got0 = orc.indexer_scores(iq, iw, neg_k, p0, ratio)
+    for r in range(T):
+        nv = min(Nc, (p0 + r + 1) // ratio)
+        assert (got0[r, :nv] == 0).all()
+
+    iq2 = rng.integers(-8, 8, (T, Hi, Di)).astype(np.int8)
+    ik2 = rng.integers(-8, 8, (Nc, Di)).astype(np.int8)
+    for h0 in range(Hi):
+        w = np.zeros((T, Hi), np.int8)
+        w[:, h0] = 1
+        got1 = orc.indexer_scores(iq2, w, ik2, p0, ratio).astype(np.int64)
+        dots = iq2[:, h0, :].astype(np.int64) @ ik2.astype(np.int64).T
+        for r in range(T):
+            nv = min(Nc, (p0 + r + 1) // ratio)
+            np.testing.assert_array_equal(got1[r, :nv], np.maximum(dots[r, :nv], 0))
+
+    iq3 = np.full((1, 4, 64), -8, np.int8)
+    ik3 = np.full((1, 64), -8, np.int8)
+    iw3 = np.full((1, 4), 4, np.int8)
+    assert int(orc.indexer_scores(iq3, iw3, ik3, 3, 4)[0, 0]) == 65536
+
+
+# ----------------------------------------------------------------- top-k pins
+def pin_topk_brute_force(orc):
+    rng = np.random.default_rng(13)
+    for trial in range(40):
+        Nc = int(rng.integers(0, 40))
+        T = 6
+        p0 = int(rng.integers(0, 4 * Nc + 8))
+        k = int(rng.integers(1, 12))
+        hi = int(rng.integers(1, 6))  # few distinct values: many ties
+        sc = rng.integers(0, hi, (T, Nc)).astype(np.int32)
+        sel, n_sel = orc.topk_select(sc, p0, 4, k, Nc)
+        for r in range(T):
+            nv = min(Nc, (p0 + r + 1) // 4)
+            want = sorted(range(nv), key=lambda j: (-int(sc[r, j]), j))[:k]
+            assert n_sel[r] == len(want)
+            assert list(sel[r, : len(want)]) == want, (trial, r)
+            assert (sel[r, len(want):] == -1).all()
+
+
+def pin_topk_closed_forms(orc):
+    Nc, k = 50, 16
+    t_last = 4 * Nc - 1  # every row visible
+    flat = np.full((1, Nc), 7, np.int32)
+    sel, n = orc.topk_select(flat, t_last, 4, k, Nc)
+    assert list(sel[0]) == list(range(k))  # all tied: lowest indices, ascending
+    inc = np.arange(Nc, dtype=np.int32)[None]
+    sel, n = orc.topk_select(inc, t_last, 4, k, Nc)
+    assert list(sel[0]) == list(range(Nc - 1, Nc - 1 - k, -1))
+    dec = (1000 - np.arange(Nc, dtype=np.int32))[None]
+    sel, n = orc.topk_select(dec, t_last, 4, k, Nc)
+    assert list(sel[0]) == list(range(k))
+    # fewer visible rows than k: all of them, padded with -1
+    sel, n = orc.topk_select(inc, 4 * 5 - 1, 4, k, Nc)
+    assert n[0] == 5 and list(sel[0, :5]) == [4, 3, 2, 1, 0] and (sel[0, 5:] == -1).all()
+    # query 0..2 sees no compressed row at all
+    sel, n = orc.topk_select(inc, 2, 4, k, Nc)
+    assert n[0] == 0 and (sel[0] == -1).all()
+
+
+def pin_topk_invariants(orc):
+    """On a tiny-256-like workload: size, order, boundary and tie rules."""
+    rng = np.random.default_rng(14)
+    inp = _tiny_inputs(rng, n_q=256, q_pos0=0, ratio=4, H=1, D=4, Hi=4, Di=64)
+    sc = orc.indexer_scores(inp["iq"], inp["iw"], inp["ik"], 0, 4)
+    k = 32
+    sel, n_sel = orc.topk_select(sc, 0, 4, k, 64)
+    for r in range(256):
+        nv = min(64, (r + 1) // 4)
+        n = int(n_sel[r])
+        assert n == min(k, nv)
+        chosen = [int(x) for x in sel[r, :n]]
+        assert len(set(chosen)) == n and all(0 <= j < nv for j in chosen)
+        s = [int(sc[r, j]) for j in chosen]
+        for a in range(n - 1):
+            assert s[a] > s[a + 1] or (s[a] == s[a + 1] and chosen[a] < chosen[a + 1])
+        rest = [j for j in range(nv) if j not in set(chosen)]
+        if rest and chosen:
+            assert max(int(sc[r, j]) for j in rest) <= s[-1]
+            ties_out = [j for j in rest if int(sc[r, j]) == s[-1]]
+            ties_in = [j for j in chosen if int(sc[r, j]) == s[-1]]
+            assert not ties_out or min(ties_out) > max(ties_in)
+
+
+# ------------------------------------------------------------- attention pins
+def _attn_brute(q, kv_comp, kv_raw, sel, n_sel, q_pos0, W, scale, d_v):
+    T, H, D = q.shape
+    out = np.zeros((T, H, d_v))
+    lse = np.zeros((T, H))
+    for r in range(T):
+        t = q_pos0 + r
+        keys = [kv_comp[int(sel[r, i])] for i in range(int(n_sel[r]))]
+        keys += [kv_raw[s] for s in range(t + 1) if t - s < W]
+        for h in range(H):
+            z = []
+            for key in keys:
+                z.append(scale * sum(float(q[r, h, d]) * float(key[d]) for d in range(D)))
+            m = max(z)
+            e = [math.exp(v - m) for v in z]
+            den = sum(e)
+            for c in range(d_v):
+                out[r, h, c] = sum(e[i] * float(keys[i][c]) for i in range(len(keys))) / den
+            lse[r, h] = m + math.log(den)
+    return out, lse
+
+
+def pin_attention_brute_force(orc):
+    rng = np.random.default_rng(15)
+    for (n_q, q_pos0, ratio, W, k, H, D, d_v) in ((10, 0, 2, 3, 2, 2, 6, 4), (6, 9, 4, 4, 3, 3, 5, 3)):
+        inp = _tiny_inputs(rng, n_q=n_q, q_pos0=q_pos0, ratio=ratio, H=H, D=D, Hi=2, Di=4)
+        nc = inp["kv_comp"].shape[0]
+        sc = orc.indexer_scores(inp["iq"], inp["iw"], inp["ik"], q_pos0, ratio)
+        sel, n_sel = orc.topk_select(sc, q_pos0, ratio, k, nc)
+        scale = 1.0 / math.sqrt(D)
+        got_o, got_l = orc.sparse_attention(inp["q"], inp["kv_comp"], inp["kv_raw"], sel, n_sel,
+                                            q_pos0, W, scale, d_v)
+        want_o, want_l = _attn_brute(inp["q"], inp["kv_comp"], inp["kv_raw"], sel, n_sel,
+                                     q_pos0, W, scale, d_v)
+        np.testing.assert_allclose(got_o, want_o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(got_l, want_l, rtol=0, atol=1e-12)
+
+
+def pin_attention_closed_forms(orc):
+    """Closed forms of softmax attention.
+
+    * query 0 sees exactly one key (its own raw row): out = that row's value
+      dims and lse = scale * q.key;
+    * q = 0: every logit is 0, out = mean of the key set's values, lse = log n;
+    * all rows identical: out = that row's values;
+    * a value column fixed to 1 returns 1 (the weights sum to one);
+    * two keys (e, 0) against q = a*e: weight of the first is a logistic.
+    """
+    rng = np.random.default_rng(16)
+    D, d_v, H, W, k, ratio = 8, 6, 3, 4, 3, 2
+    inp = _tiny_inputs(rng, n_q=12, q_pos0=0, ratio=ratio, H=H, D=D, Hi=2, Di=4)
+    nc = inp["kv_comp"].shape[0]
+    sc = orc.indexer_scores(inp["iq"], inp["iw"], inp["ik"], 0, ratio)
+    sel, n_sel = orc.topk_select(sc, 0, ratio, k, nc)
+    scale = 0.37
+    out, lse = orc.sparse_attention(inp["q"], inp["kv_comp"], inp["kv_raw"], sel, n_sel, 0, W,
+                                    scale, d_v)
+    x0 = inp["kv_raw"][0].astype(np.float64)
+    np.testing.assert_array_equal(out[0], np.broadcast_to(x0[:d_v], (H, d_v)))
+    np.testing.assert_allclose(lse[0], scale * (inp["q"][0].astype(np.float64) @ x0), atol=1e-12)
+
+    qz = np.zeros_like(inp["q"])
+    out, lse = orc.sparse_attention(qz, inp["kv_comp"], inp["kv_raw"], sel, n_sel, 0, W, scale, d_v)
+    for r in range(12):
+        keys = [inp["kv_comp"][int(sel[r, i])] for i in range(int(n_sel[r]))]
+        keys += [inp["kv_raw"][s] for s in range(max(0, r - W + 1), r + 1)]
+        mean = np.mean(np.array(keys, dtype=np.float64)[:, :d_v], axis=0)
+        np.testing.assert_allclose(out[r], np.broadcast_to(mean, (H, d_v)), atol=1e-12)
+        np.testing.assert_allclose(lse[r], math.log(len(keys)), atol=1e-12)
+
+    v = rng.standard_normal(D).astype(np.float16)
+    same_raw = np.broadcast_to(v, inp["kv_raw"].shape).copy()
+    same_comp = np.broadcast_to(v, inp["kv_comp"].shape).copy()
+    out, _ = orc.sparse_attention(inp["q"], same_comp, same_raw, sel, n_sel, 0, W, scale, d_v)
+    np.testing.assert_allclose(out, np.broadcast_to(v[:d_v].astype(np.float64), out.shape),
+                               atol=1e-12)
+
+    ones_raw = inp["kv_raw"].copy()
+    ones_comp = inp["kv_comp"].copy()
+    ones_raw[:, 2] = 1.0
+    ones_comp[:, 2] = 1.0
+    out, _ = orc.sparse_attention(inp["q"], ones_comp, ones_raw, sel, n_sel, 0, W, scale, d_v)
+    np.testing.assert_allclose(out[:, :, 2], 1.0, atol=1e-12)
+
+    a = 1.75  # exact in fp16
+    q2 = np.zeros((2, 1, D), np.float16)
+    q2[1, 0, 0] = a
+    raw2 = np.zeros((2, D), np.float16)
+    raw2[0, 0] = 1.0  # key 0 = e0, key 1 = 0; both in query 1's window
+    comp2 = np.zeros((0, D), np.float16)
+    sel2 = np.full((2, 1), -1, np.int32)
+    out, lse = orc.sparse_attention(q2, comp2, raw2, sel2, np.zeros(2, np.int32), 0, 2, scale, D)
+    w0 = 1.0 / (1.0 + math.exp(-scale * a))
+    np.testing.assert_allclose(out[1, 0, 0], w0, atol=1e-12)
+    np.testing.assert_allclose(lse[1, 0], math.log(math.exp(scale * a) + 1.0), atol=1e-12)
+
+
+def pin_sparse_equals_dense_sdpa(orc):
+    """When k covers every visible compressed row, the sparse layer equals
+    dense causal attention over [compressed ; raw] keys with an explicit
+    boolean mask, computed by torch's scaled_dot_product_attention in fp64."""
+    import torch
+
+    rng = np.random.default_rng(17)
+    n_q, q_pos0, ratio, W, H, D, d_v = 24, 9, 4, 5, 4, 16, 12
+    inp = _tiny_inputs(rng, n_q=n_q, q_pos0=q_pos0, ratio=ratio, H=H, D=D, Hi=4, Di=8)
+    nc = inp["kv_comp"].shape[0]
+    k = nc  # covers every visible row
+    sc = orc.indexer_scores(inp["iq"], inp["iw"], inp["ik"], q_pos0, ratio)
+    sel, n_sel = orc.topk_select(sc, q_pos0, ratio, k, nc)
+    scale = 1.0 / math.sqrt(D)
+    got, _ = orc.sparse_attention(inp["q"], inp["kv_comp"], inp["kv_raw"], sel, n_sel, q_pos0, W,
+                                  scale, d_v)
+    n_raw = inp["kv_raw"].shape[0]
+    keys = np.concatenate([inp["kv_comp"], inp["kv_raw"]]).astype(np.float64)
+    mask = np.zeros((n_q, nc + n_raw), dtype=bool)
+    for r in range(n_q):
+        t = q_pos0 + r
+        for j in range(nc):
+            mask[r, j] = all(ratio * j + m <= t for m in range(ratio))
+        for s in range(n_raw):
+            mask[r, nc + s] = s <= t and t - s < W
+    qt = torch.from_numpy(inp["q"].astype(np.float64)).permute(1, 0, 2).contiguous()  # [H, T, D]
+    kt = torch.from_numpy(keys)[None].expand(H, -1, -1).contiguous()
+    vt = torch.from_numpy(keys[:, :d_v].copy())[None].expand(H, -1, -1).contiguous()
+    mt = torch.from_numpy(mask)[None].expand(H, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=scale)
+    ref = ref.permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def pin_band_independence(orc):
+    """Each band run as its own call (its own q_pos0, history cut at the band's
+    last query) gives the same result as one call over all queries: bands
+    only schedule work ("perf(ds4): extend sparse prefill scheduling to 10K",
+    Summary: independent 2K attention bands), and rows after the last query
+    cannot matter (causality)."""
+    rng = np.random.default_rng(18)
+    n_q, q_pos0, ratio, band = 40, 6, 4, 16
+    inp = _tiny_inputs(rng, n_q=n_q, q_pos0=q_pos0, ratio=ratio, H=2, D=8, Hi=4, Di=16)
+    kw = dict(ratio=ratio, window=5, top_k=3, scale=0.3, d_v=6)
+    full = orc.prefill(inp, q_pos0=q_pos0, **kw)
+    parts = []
+    for a in range(0, n_q, band):
+        b = min(n_q, a + band)
+        n_raw_b = q_pos0 + b
+        nc_b = n_raw_b // ratio
+        sub = {
+            "q": inp["q"][a:b], "iq": inp["iq"][a:b], "iw": inp["iw"][a:b],
+            "kv_raw": inp["kv_raw"][:n_raw_b], "kv_comp": inp["kv_comp"][:nc_b],
+            "ik": inp["ik"][:nc_b],
+        }
+        parts.append(orc.prefill(sub, q_pos0=q_pos0 + a, chunk=5, **kw))
+    for key in ("sel", "n_sel", "out", "lse"):
+        np.testing.assert_array_equal(full[key], np.concatenate([p[key] for p in parts]))
+
+
+PINS = [
+    pin_visibility_brute_force,
+    pin_window_brute_force,
+    pin_mask_memory,
+    pin_indexer_brute_force,
+    pin_indexer_closed_forms,
+    pin_topk_brute_force,
+    pin_topk_closed_forms,
+    pin_topk_invariants,
+    pin_attention_brute_force,
+    pin_attention_closed_forms,
+    pin_sparse_equals_dense_sdpa,
+    pin_band_independence,
+]
