@@ -1,0 +1,271 @@
+// C ABI of the sparse-MLA prefill library: argument checks, workspace
+// sizing and the band schedule. Every check runs on the host before any HIP
+// call, so a rejected call enqueues nothing (and needs no GPU).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/spmla.h"
+#include "spmla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SPMLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks every rule that does not involve a pointer.
+int check_desc(const spmla_desc* d) {
+  if (!d) return fail(SPMLA_EINVAL, "desc is NULL");
+  if (d->n_q < 0) return fail(SPMLA_EINVAL, "n_q=%d < 0", d->n_q);
+  if (d->q_pos0 < 0) return fail(SPMLA_EINVAL, "q_pos0=%d < 0", d->q_pos0);
+  if (d->ratio < 1) return fail(SPMLA_EINVAL, "ratio=%d < 1", d->ratio);
+  if (d->window < 1) return fail(SPMLA_EINVAL, "window=%d < 1", d->window);
+  if (d->top_k < 1) return fail(SPMLA_EINVAL, "top_k=%d < 1", d->top_k);
+  if (d->band < 1) return fail(SPMLA_EINVAL, "band=%d < 1", d->band);
+  if (d->n_heads < 1 || d->d_qk < 1 || d->d_v < 1 || d->idx_heads < 1 || d->idx_dim < 1)
+    return fail(SPMLA_EINVAL, "head counts and widths must be >= 1");
+  if (d->d_v > d->d_qk) return fail(SPMLA_EINVAL, "d_v=%d > d_qk=%d", d->d_v, d->d_qk);
+  if ((int64_t)d->n_raw < (int64_t)d->q_pos0 + d->n_q)
+    return fail(SPMLA_EINVAL, "n_raw=%d < q_pos0+n_q=%lld", d->n_raw,
+                (long long)d->q_pos0 + d->n_q);
+  if (d->n_comp != d->n_raw / d->ratio)
+    return fail(SPMLA_EINVAL, "n_comp=%d != floor(n_raw/ratio)=%d", d->n_comp, d->n_raw / d->ratio);
+  if (!std::isfinite(d->scale)) return fail(SPMLA_EINVAL, "scale is not finite");
+  if (d->n_heads != spmla::kHeads || d->d_qk != spmla::kDqk || d->d_v != spmla::kDv)
+    return fail(SPMLA_EUNSUPPORTED, "kernels cover n_heads=16, d_qk=576, d_v=512 (got %d, %d, %d)",
+                d->n_heads, d->d_qk, d->d_v);
+  if (d->idx_heads != spmla::kIdxHeads || d->idx_dim != spmla::kIdxDim)
+    return fail(SPMLA_EUNSUPPORTED, "kernels cover idx_heads=4, idx_dim=64 (got %d, %d)",
+                d->idx_heads, d->idx_dim);
+  if (d->top_k > spmla::kMaxTopK)
+    return fail(SPMLA_EUNSUPPORTED, "top_k=%d > %d", d->top_k, spmla::kMaxTopK);
+  if (d->n_comp > spmla::kMaxComp)
+    return fail(SPMLA_EUNSUPPORTED, "n_comp=%d > %d", d->n_comp, spmla::kMaxComp);
+  return SPMLA_OK;
+}
+
+#define REQUIRE_PTR(p)                                                              \
+  do {                                                                              \
+    if (!(p)) return fail(SPMLA_EINVAL, "%s is NULL", #p);                          \
+    if (!aligned16(p)) return fail(SPMLA_EINVAL, "%s is not 16-byte aligned", #p);  \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                             \
+  do {                                                                              \
+    if ((p) && !aligned16(p)) return fail(SPMLA_EINVAL, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPMLA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t scores_bytes_per_band(const spmla_desc* d) {
+  const int64_t rows = d->band < d->n_q ? d->band : d->n_q;
+  return (size_t)rows * (size_t)d->n_comp * sizeof(int32_t);
+}
+size_t sel_bytes_per_band(const spmla_desc* d) {
+  const int64_t rows = d->band < d->n_q ? d->band : d->n_q;
+  return (size_t)rows * (size_t)d->top_k * sizeof(int32_t);
+}
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
+                          const uint16_t* kv_raw, const int32_t* sel, float* out, float* lse) {
+  spmla::AttnArgs a;
+  a.q = reinterpret_cast<const _Float16*>(q);
+  a.kv_comp = reinterpret_cast<const _Float16*>(kv_comp);
+  a.kv_raw = reinterpret_cast<const _Float16*>(kv_raw);
+  a.sel = sel;
+  a.out = out;
+  a.lse = lse;
+  a.n_q = d->n_q;
+  a.q_pos0 = d->q_pos0;
+  a.n_comp = d->n_comp;
+  a.n_raw = d->n_raw;
+  a.ratio = d->ratio;
+  a.window = d->window;
+  a.top_k = d->top_k;
+  a.scale_log2e = (float)((double)d->scale * 1.4426950408889634);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spmla_last_error(void) { return g_last_error.c_str(); }
+
+int spmla_abi_version(void) { return 1; }
+
+int spmla_check_desc(const spmla_desc* desc) {
+  const int rc = check_desc(desc);
+  return rc ? rc : ok();
+}
+
+int spmla_num_bands(const spmla_desc* desc) {
+  const int rc = check_desc(desc);
+  if (rc) return rc;
+  ok();
+  return (int)(((int64_t)desc->n_q + desc->band - 1) / desc->band);
+}
+
+int spmla_indexer_scores(const spmla_desc* d, const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                         int32_t* scores, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->n_q == 0) return ok();
+  REQUIRE_PTR(iq);
+  REQUIRE_PTR(iw);
+  if (d->n_comp > 0) {
+    REQUIRE_PTR(ik);
+    REQUIRE_PTR(scores);
+  }
+  spmla::IndexerArgs a;
+  a.iq = iq;
+  a.iw = iw;
+  a.ik = ik;
+  a.scores = scores;
+  a.ld_scores = d->n_comp;
+  a.n_q = d->n_q;
+  a.q_pos0 = d->q_pos0;
+  a.n_comp = d->n_comp;
+  a.ratio = d->ratio;
+  return hip_status(spmla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
+}
+
+int spmla_topk(const spmla_desc* d, const int32_t* scores, int32_t* sel, int32_t* n_sel,
+               void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->n_q == 0) return ok();
+  if (d->n_comp > 0) REQUIRE_PTR(scores);
+  REQUIRE_PTR(sel);
+  OPTIONAL_PTR(n_sel);
+  spmla::TopkArgs a;
+  a.scores = scores;
+  a.ld_scores = d->n_comp;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.n_q = d->n_q;
+  a.q_pos0 = d->q_pos0;
+  a.n_comp = d->n_comp;
+  a.ratio = d->ratio;
+  a.top_k = d->top_k;
+  return hip_status(spmla::launch_topk(a, (hipStream_t)stream), "top-k launch");
+}
+
+int spmla_sparse_attn(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
+                      const uint16_t* kv_raw, const int32_t* sel, float* out, float* lse,
+                      void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->n_q == 0) return ok();
+  REQUIRE_PTR(q);
+  if (d->n_comp > 0) REQUIRE_PTR(kv_comp);
+  REQUIRE_PTR(kv_raw);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(lse);
+  const spmla::AttnArgs a = attn_args(d, q, kv_comp, kv_raw, sel, out, lse);
+  return hip_status(spmla::launch_attn(a, (hipStream_t)stream), "attention launch");
+}
+
+int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!bytes) return fail(SPMLA_EINVAL, "bytes is NULL");
+  *bytes = round_up(scores_bytes_per_band(d), 256) + round_up(sel_bytes_per_band(d), 256);
+  return ok();
+}
+
+int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
+                  const uint16_t* kv_raw, const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                  float* out, float* lse, int32_t* sel_out, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->n_q == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv_raw);
+  REQUIRE_PTR(iq);
+  REQUIRE_PTR(iw);
+  if (d->n_comp > 0) {
+    REQUIRE_PTR(kv_comp);
+    REQUIRE_PTR(ik);
+  }
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(lse);
+  OPTIONAL_PTR(sel_out);
+  size_t need = 0;
+  spmla_prefill_workspace_bytes(d, &need);
+  if (workspace_bytes < need)
+    return fail(SPMLA_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  REQUIRE_PTR(workspace);
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* band_scores = reinterpret_cast<int32_t*>(ws);
+  int32_t* band_sel = reinterpret_cast<int32_t*>(ws + round_up(scores_bytes_per_band(d), 256));
+
+  for (int64_t b0 = 0; b0 < d->n_q; b0 += d->band) {
+    const int bn = (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band);
+    const int pos0 = d->q_pos0 + (int)b0;
+    int32_t* sel = sel_out ? sel_out + b0 * d->top_k : band_sel;
+
+    if (d->n_comp > 0) {
+      spmla::IndexerArgs ia;
+      ia.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
+      ia.iw = iw + b0 * spmla::kIdxHeads;
+      ia.ik = ik;
+      ia.scores = band_scores;
+      ia.ld_scores = d->n_comp;
+      ia.n_q = bn;
+      ia.q_pos0 = pos0;
+      ia.n_comp = d->n_comp;
+      ia.ratio = d->ratio;
+      rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
+      if (rc) return rc;
+    }
+    spmla::TopkArgs ta;
+    ta.scores = band_scores;
+    ta.ld_scores = d->n_comp;
+    ta.sel = sel;
+    ta.n_sel = nullptr;
+    ta.n_q = bn;
+    ta.q_pos0 = pos0;
+    ta.n_comp = d->n_comp;
+    ta.ratio = d->ratio;
+    ta.top_k = d->top_k;
+    rc = hip_status(spmla::launch_topk(ta, st), "top-k launch");
+    if (rc) return rc;
+
+    spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
+                                   out + b0 * spmla::kHeads * spmla::kDv,
+                                   lse ? lse + b0 * spmla::kHeads : nullptr);
+    aa.n_q = bn;
+    aa.q_pos0 = pos0;
+    rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every function include/spmla.h declares, and its
+argument checks reject bad calls before anything reaches the HIP runtime.
+"""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_long_context_int8_amd as sp
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spmla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spmla_[a-z_]+)\s*\(", text)))
+
+
+def desc_of(w, **kw):
+    d = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sp.load_library()
+    decl = declared_functions()
+    assert decl == sorted(sp.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", sp.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (spmla_\w+)", out.stdout))
+    for name in decl:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version():
+    assert sp.spmla_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    # 13 int32 fields then one float, no padding.
+    assert ctypes.sizeof(sp.spmla_desc) == 14 * 4
+    assert sp.spmla_desc.scale.offset == 13 * 4
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=[w.name for w in workloads.WORKLOADS])
+def test_workload_descriptors_are_valid(w):
+    assert sp.spmla_check_desc(desc_of(w)) == 0
+
+
+BAD = [
+    (dict(n_q=-1), sp.SPMLA_EINVAL, "n_q"),
+    (dict(q_pos0=-5), sp.SPMLA_EINVAL, "q_pos0"),
+    (dict(ratio=0), sp.SPMLA_EINVAL, "ratio"),
+    (dict(window=0), sp.SPMLA_EINVAL, "window"),
+    (dict(top_k=0), sp.SPMLA_EINVAL, "top_k"),
+    (dict(band=0), sp.SPMLA_EINVAL, "band"),
+    (dict(n_raw=100), sp.SPMLA_EINVAL, "n_raw"),
+    (dict(n_comp=63), sp.SPMLA_EINVAL, "n_comp"),
+    (dict(d_v=600), sp.SPMLA_EINVAL, "d_v"),
+    (dict(scale=float("nan")), sp.SPMLA_EINVAL, "scale"),
+    (dict(n_heads=8), sp.SPMLA_EUNSUPPORTED, "n_heads"),
+    (dict(d_qk=512, d_v=512), sp.SPMLA_EUNSUPPORTED, "d_qk"),
+    (dict(idx_dim=32), sp.SPMLA_EUNSUPPORTED, "idx_dim"),
+    (dict(top_k=4097), sp.SPMLA_EUNSUPPORTED, "top_k"),
+]
+
+
+@pytest.mark.parametrize("kw,code,word", BAD, ids=[b[2] for b in BAD])
+def test_bad_descriptor_rejected(kw, code, word):
+    d = desc_of(workloads.TINY_256, **kw)
+    with pytest.raises(sp.SpmlaError) as e:
+        sp.spmla_check_desc(d)
+    assert e.value.code == code
+    assert word in str(e.value)
+
+
+def test_too_many_compressed_rows_unsupported():
+    d = sp.make_desc(8, 131072, 128, 512)  # n_comp = 32770
+    with pytest.raises(sp.SpmlaError) as e:
+        sp.spmla_check_desc(d)
+    assert e.value.code == sp.SPMLA_EUNSUPPORTED
+
+
+def test_band_schedule_matches_pages():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "band_schedule.json")))
+    for case in g["cases"]:
+        T = case["tokens"]
+        d = sp.make_desc(T, 0, 128, 512, band=g["band"])
+        nb = sp.spmla_num_bands(d)
+        assert nb == case["bands"]
+        assert T - (nb - 1) * g["band"] == case["last_band"]
+    assert g["max_bands"] * g["band"] == g["frontier_printed"]
+
+
+def test_workspace_bytes():
+    w = workloads.PREFILL_8192
+    d = desc_of(w)
+    nb = sp.spmla_prefill_workspace_bytes(d)
+    assert nb == 2048 * 2048 * 4 + 2048 * 512 * 4
+    w4 = workloads.CHUNK_8192_AT_114687
+    nb4 = sp.spmla_prefill_workspace_bytes(desc_of(w4))
+    assert nb4 >= 2048 * 30719 * 4 + 2048 * 2048 * 4
+
+
+A = 1 << 20  # an aligned fake address; never dereferenced by these calls
+
+
+def _call_prefill(lib, d, ptrs, ws_bytes):
+    return lib.spmla_prefill(ctypes.byref(d), *[ctypes.c_void_p(p) for p in ptrs],
+                             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    lib = sp.load_library()
+    d = desc_of(workloads.TINY_256)
+    good = [A] * 10  # q kv_comp kv_raw iq iw ik out lse sel ws
+    for i, name in enumerate(["q", "kv_comp", "kv_raw", "iq", "iw", "ik", "out"]):
+        ptrs = list(good)
+        ptrs[i] = 0
+        assert _call_prefill(lib, d, ptrs, 1 << 30) == sp.SPMLA_EINVAL
+        assert name in lib.spmla_last_error().decode()
+        ptrs[i] = A + 4
+        assert _call_prefill(lib, d, ptrs, 1 << 30) == sp.SPMLA_EINVAL
+        assert "aligned" in lib.spmla_last_error().decode()
+    assert _call_prefill(lib, d, good, 0) == sp.SPMLA_EWORKSPACE
+    assert lib.spmla_sparse_attn(ctypes.byref(d), None, None, None, None, None, None, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_topk(ctypes.byref(d), None, None, None, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_indexer_scores(ctypes.byref(d), None, None, None, None, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_check_desc(None) == sp.SPMLA_EINVAL
+
+
+def test_empty_call_is_a_noop():
+    lib = sp.load_library()
+    d = sp.make_desc(0, 10, 64, 32)
+    assert _call_prefill(lib, d, [0] * 10, 0) == 0
+    assert lib.spmla_sparse_attn(ctypes.byref(d), None, None, None, None, None, None, None) == 0
+    assert lib.spmla_last_error().decode() == ""
+
+
+def test_generator_shapes_and_ranges():
+    w = workloads.TINY_256
+    x = workloads.generate(w)
+    assert x["q"].shape == (256, 16, 576) and x["q"].dtype.name == "float16"
+    assert x["kv_raw"].shape == (256, 576)
+    assert x["kv_comp"].shape == (64, 576)
+    assert x["iq"].shape == (256, 4, 64) and x["iq"].min() >= -8 and x["iq"].max() <= 7
+    assert x["ik"].shape == (64, 64)
+    assert x["iw"].shape == (256, 4) and x["iw"].min() >= 1 and x["iw"].max() <= 4
+    y = workloads.generate(w)
+    for k in x:
+        assert (x[k] == y[k]).all()  # seeded

@@ -1,0 +1,272 @@
+"""HIP path against the CPU oracle, called through the C ABI (needs a GPU).
+
+Bar: selected indices and indexer scores bit-exact; attention outputs within
+max-abs 2e-3 and NMSE 1e-6 of the fp64 oracle over each compared tensor.
+Full-size workloads run in the same launch configuration as the benchmark
+(spmla_prefill, 2,048-query bands) and are compared on sampled queries that
+the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-3
+MAX_NMSE = 1e-6
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sp():
+    import torch
+
+    import sparse_long_context_int8_amd as sp
+
+    assert torch.cuda.is_available()
+    sp.load_library()
+    return sp
+
+
+def to_dev(x):
+    import torch
+
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+
+
+def desc_of(sp, w, **kw):
+    d = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def assert_close(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    max_abs = float(err.max()) if err.size else 0.0
+    nmse = float((err ** 2).sum() / max((want ** 2).sum(), 1e-300)) if err.size else 0.0
+    say(f"  {what}: max_abs={max_abs:.3e} nmse={nmse:.3e}")
+    assert np.isfinite(got).all(), what
+    assert max_abs <= MAX_ABS, (what, max_abs)
+    assert nmse <= MAX_NMSE, (what, nmse)
+
+
+def run_steps(sp, w, x, dev, d=None):
+    """Indexer, top-k and attention as three separate ABI calls."""
+    import torch
+
+    d = d or desc_of(sp, w)
+    scores = torch.empty((w.n_q, w.n_comp), dtype=torch.int32, device="cuda")
+    sel = torch.empty((w.n_q, w.top_k), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((w.n_q,), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.n_q, 16, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.n_q, 16), dtype=torch.float32, device="cuda")
+    sp.spmla_indexer_scores(d, dev["iq"], dev["iw"], dev["ik"], scores)
+    sp.spmla_topk(d, scores, sel, n_sel)
+    sp.spmla_sparse_attn(d, dev["q"], dev["kv_comp"], dev["kv_raw"], sel, out, lse)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), sel.cpu().numpy(), n_sel.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+
+
+# ------------------------------------------------------------- small, whole
+@pytest.mark.parametrize("name", ["tiny-256", "band-2048"])
+def test_steps_match_oracle(sp, name):
+    w = workloads.BY_NAME[name]
+    say(f"[parity steps] {name}")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    scores, sel, n_sel, out, lse = run_steps(sp, w, x, dev)
+    want_scores = oracle.indexer_scores(x["iq"], x["iw"], x["ik"], w.q_pos0, w.ratio)
+    np.testing.assert_array_equal(scores, want_scores)
+    want_sel, want_nsel = oracle.topk_select(want_scores, w.q_pos0, w.ratio, w.top_k, w.n_comp)
+    np.testing.assert_array_equal(sel, want_sel)
+    np.testing.assert_array_equal(n_sel, want_nsel)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    assert_close(out, ref["out"], f"{name} out")
+    assert_close(lse, ref["lse"], f"{name} lse")
+
+
+@pytest.mark.parametrize("name", ["tiny-256", "band-2048"])
+def test_prefill_matches_oracle(sp, name):
+    w = workloads.BY_NAME[name]
+    say(f"[parity prefill] {name}")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    import torch
+
+    torch.cuda.synchronize()
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"{name} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"{name} lse")
+
+
+# ------------------------------------------------------ full size, sampled
+def sample_rows(w, n=48, seed=0):
+    rng = np.random.default_rng(1000 + seed)
+    rows = {0, 1, 2, 3, 4, w.n_q - 1, w.n_q - 2}
+    for b in range(0, w.n_q, w.band):  # both sides of every band edge
+        rows.update({b, max(0, b - 1), min(w.n_q - 1, b + 1)})
+    rows.update(int(v) for v in rng.integers(0, w.n_q, n))
+    return sorted(r for r in rows if 0 <= r < w.n_q)
+
+
+@pytest.mark.parametrize("name", ["prefill-8192", "prefill-9133", "chunk-8192-after-114687"])
+def test_full_size_prefill_sampled(sp, name):
+    import torch
+
+    w = workloads.BY_NAME[name]
+    say(f"[parity full] {name}: generating")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    say(f"[parity full] {name}: running spmla_prefill")
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rows = sample_rows(w)
+    say(f"[parity full] {name}: oracle on {len(rows)} sampled queries")
+    want_out, want_lse, got_out, got_lse = [], [], [], []
+    for r in rows:
+        ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                             scale=w.scale, d_v=w.d_v, q_begin=r, q_end=r + 1)
+        np.testing.assert_array_equal(sel[r], ref["sel"][0], err_msg=f"sel row {r}")
+        want_out.append(ref["out"][0]), want_lse.append(ref["lse"][0])
+        got_out.append(out[r]), got_lse.append(lse[r])
+    assert_close(np.array(got_out), np.array(want_out), f"{name} out[sampled]")
+    assert_close(np.array(got_lse), np.array(want_lse), f"{name} lse[sampled]")
+
+
+# ------------------------------------------------------------- properties
+def test_deterministic_and_band_invariant(sp):
+    import torch
+
+    w = workloads.PREFILL_9133
+    say("[parity] determinism and band invariance, prefill-9133")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    o1, l1, s1 = sp.prefill(desc_of(sp, w), dev)
+    o2, l2, s2 = sp.prefill(desc_of(sp, w), dev)
+    o3, l3, s3 = sp.prefill(desc_of(sp, w, band=1000), dev)
+    o4, l4, s4 = sp.prefill(desc_of(sp, w, band=w.n_q), dev)
+    torch.cuda.synchronize()
+    for o, l, s in ((o2, l2, s2), (o3, l3, s3), (o4, l4, s4)):
+        assert torch.equal(o1, o), "out differs"
+        assert torch.equal(l1, l), "lse differs"
+        assert torch.equal(s1, s), "sel differs"
+
+
+def test_first_query_is_its_own_row(sp):
+    """Query 0 sees one key (its own raw row): softmax weight exactly 1."""
+    import torch
+
+    w = workloads.TINY_256
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    out, lse, _ = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    x0 = x["kv_raw"][0].astype(np.float32)
+    np.testing.assert_array_equal(out[0].cpu().numpy(), np.broadcast_to(x0[:512], (16, 512)))
+
+
+EDGE = [
+    # name, shape
+    ("one-query", workloads.LayerShape("e1", n_q=1, q_pos0=37, window=8, top_k=5)),
+    ("no-compressed-rows", workloads.LayerShape("e2", n_q=3, q_pos0=0, window=4, top_k=8)),
+    ("k-exceeds-visible", workloads.LayerShape("e3", n_q=70, q_pos0=100, window=16, top_k=4096)),
+    ("ragged-tiles", workloads.LayerShape("e4", n_q=133, q_pos0=61, window=7, top_k=17, band=50)),
+    ("window-1", workloads.LayerShape("e5", n_q=40, q_pos0=9, window=1, top_k=3)),
+    ("long-history-few-queries",
+     workloads.LayerShape("e6", n_q=21, q_pos0=131000 - 21, window=128, top_k=2048)),
+]
+
+
+@pytest.mark.parametrize("name,w", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(sp, name, w):
+    say(f"[parity edge] {name}")
+    x = workloads.generate(w, seed=7)
+    dev = to_dev(x)
+    scores, sel, n_sel, out, lse = run_steps(sp, w, x, dev)
+    want_scores = oracle.indexer_scores(x["iq"], x["iw"], x["ik"], w.q_pos0, w.ratio)
+    np.testing.assert_array_equal(scores, want_scores)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    np.testing.assert_array_equal(sel, ref["sel"])
+    np.testing.assert_array_equal(n_sel, ref["n_sel"])
+    assert_close(out, ref["out"], f"{name} out")
+    assert_close(lse, ref["lse"], f"{name} lse")
+    import sparse_long_context_int8_amd as spm
+
+    o2, l2, s2 = spm.prefill(desc_of(sp, w), dev)
+    np.testing.assert_array_equal(s2.cpu().numpy(), ref["sel"])
+    assert_close(o2.cpu().numpy(), ref["out"], f"{name} prefill out")
+
+
+def test_topk_heavy_ties(sp):
+    """Scores from a handful of values: the index tie-break decides most rows."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    for (n_q, q_pos0, k, hi) in ((64, 4000, 100, 3), (32, 120000, 2048, 7), (16, 50, 4, 1)):
+        n_comp = (q_pos0 + n_q) // 4
+        d = sp.make_desc(n_q, q_pos0, 16, k)
+        sc = rng.integers(0, hi + 1, (n_q, n_comp)).astype(np.int32) * 3 - 1
+        for r in range(n_q):
+            sc[r, oracle.n_visible(q_pos0 + r, n_comp, 4):] = oracle.INVISIBLE
+        sel = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+        n_sel = torch.empty((n_q,), dtype=torch.int32, device="cuda")
+        sp.spmla_topk(d, torch.from_numpy(sc).cuda(), sel, n_sel)
+        torch.cuda.synchronize()
+        want, want_n = oracle.topk_select(sc, q_pos0, 4, k, n_comp)
+        np.testing.assert_array_equal(sel.cpu().numpy(), want)
+        np.testing.assert_array_equal(n_sel.cpu().numpy(), want_n)
+
+
+def test_topk_extreme_scores(sp):
+    """Full int32 range (the largest and smallest real scores) and negatives."""
+    import torch
+
+    rng = np.random.default_rng(6)
+    n_q, q_pos0, k = 8, 2000, 64
+    n_comp = (q_pos0 + n_q) // 4
+    sc = rng.integers(-(2**31) + 1, 2**31 - 1, (n_q, n_comp), dtype=np.int64).astype(np.int32)
+    sc[:, 5] = 2**31 - 1
+    sc[:, 6] = -(2**31) + 1
+    for r in range(n_q):
+        sc[r, oracle.n_visible(q_pos0 + r, n_comp, 4):] = oracle.INVISIBLE
+    d = sp.make_desc(n_q, q_pos0, 16, k)
+    sel = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    sp.spmla_topk(d, torch.from_numpy(sc).cuda(), sel, None)
+    torch.cuda.synchronize()
+    want, _ = oracle.topk_select(sc, q_pos0, 4, k, n_comp)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want)
+
+
+def test_lse_natural_log(sp):
+    """q = 0 makes every logit 0, so lse = log(number of keys) exactly-ish."""
+    import torch
+
+    w = workloads.LayerShape("z", n_q=50, q_pos0=300, window=32, top_k=40)
+    x = workloads.generate(w, seed=3)
+    x["q"][:] = 0
+    dev = to_dev(x)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    for r in range(w.n_q):
+        t = w.q_pos0 + r
+        nk = min(w.top_k, oracle.n_visible(t, w.n_comp, 4)) + min(w.window, t + 1)
+        np.testing.assert_allclose(lse[r].cpu().numpy(), math.log(nk), atol=1e-5)
