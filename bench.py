@@ -1,0 +1,276 @@
+"""Benchmark: sparse-MLA prefill tokens/s per layer on one MI355X.
+
+One step = one spmla_prefill call over the 8,192-token prefill workload
+(four 2,048-query bands: indexer -> top-k -> streaming attention per band),
+inputs resident in HBM. Prints one JSON line:
+  value      whole-job tokens/s over the timed steps
+  roofline   the attention kernel (dominant) against the HBM roofline, with
+             algorithmic bytes per launch and its live launch duration
+  cpu_baseline  the CPU oracle timed on the host cores on a bounded sample
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix
+METRIC = "sparse-MLA prefill tokens/s per layer; % of HBM/MFMA roofline"
+ATTN_SRC = os.path.join(ROOT, "sparse_long_context_int8_amd", "csrc", "attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def keys_per_query(w):
+    """(n_sel, n_win) of every query of the workload (analytic visibility)."""
+    t = w.q_pos0 + np.arange(w.n_q, dtype=np.int64)
+    n_vis = np.minimum(w.n_comp, (t + 1) // w.ratio)
+    n_sel = np.minimum(w.top_k, n_vis)
+    n_win = np.minimum(w.window, t + 1)
+    return n_sel, n_win
+
+
+def attn_bytes_per_query(w):
+    """Algorithmic HBM bytes of the attention step for each query: every
+    selected and window row gathered once (d_qk fp16), the query (16 x d_qk
+    fp16), the output (16 x d_v fp32) and lse, and the selected indices read."""
+    n_sel, n_win = keys_per_query(w)
+    row = w.d_qk * 2
+    return (row * (n_sel + n_win) + w.n_heads * w.d_qk * 2 + w.n_heads * w.d_v * 4
+            + w.n_heads * 4 + 4 * n_sel)
+
+
+def attn_flops_per_query(w):
+    n_sel, n_win = keys_per_query(w)
+    return 2.0 * w.n_heads * (w.d_qk + w.d_v) * (n_sel + n_win)
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"attn_kernel-{workload_name}-hbm-traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"attn\.hip sha256\[:16\]:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash(ATTN_SRC):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, x):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle  # test infrastructure: used only for this baseline leg
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    # Whole workload if it is the 8,192-token prefill (about 10-15 s on
+    # 8-16 host cores); otherwise the first 1,024 queries of the last band.
+    if w.n_q <= 8192 and w.q_pos0 == 0:
+        a, b = 0, w.n_q
+    else:
+        a = ((w.n_q - 1) // w.band) * w.band
+        b = min(w.n_q, a + 1024)
+    c0 = time.process_time()
+    t0 = time.perf_counter()
+    oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                   scale=w.scale, d_v=w.d_v, q_begin=a, q_end=b)
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {
+        "value": (b - a) / wall,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"queries [{a}, {b}) of {w.name} (numpy fp64 oracle, whole layer)",
+        "wall_s": round(wall, 3),
+        "cpu_s": round(cpu, 3),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill-8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the prefill bands of one layer fit a single "
+              f"MI355X and no multi-GPU path is built (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import sparse_long_context_int8_amd as sp
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    if args.copy_mib:
+        # Reference dispatch for byte counters: reads and writes exactly
+        # copy_mib MiB each.
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mib, "dispatches": 3}), flush=True)
+        return
+    sp.load_library()
+    w = workloads.BY_NAME[args.workload]
+    log(f"workload {w.name}: generating inputs")
+    x = workloads.generate(w)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in x.items()}
+    desc = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
+    out = torch.empty((w.n_q, w.n_heads, w.d_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.n_q, w.n_heads), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.n_q, w.top_k), dtype=torch.int32, device="cuda")
+    ws_bytes = sp.spmla_prefill_workspace_bytes(desc)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sp.spmla_prefill(desc, dev["q"], dev["kv_comp"], dev["kv_raw"], dev["iq"], dev["iw"],
+                         dev["ik"], out, lse, sel, ws, ws_bytes)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    ms_per_step = total_ms / args.steps
+    value = w.n_q * args.steps / (total_ms / 1e3)
+
+    # Per-kernel launch durations, same launch configuration (one band per
+    # launch) on the same stream, HIP events between the launches.
+    log("per-kernel breakdown")
+    n_bands = sp.spmla_num_bands(desc)
+    scores_b = torch.empty((min(w.band, w.n_q), w.n_comp), dtype=torch.int32, device="cuda")
+    ev = {k: [] for k in ("indexer", "topk", "attn")}
+    reps = max(3, args.steps // 2)
+    for _ in range(reps):
+        for b in range(n_bands):
+            a0 = b * w.band
+            bn = min(w.band, w.n_q - a0)
+            d = sp.make_desc(bn, w.q_pos0 + a0, w.window, w.top_k, ratio=w.ratio, band=w.band,
+                             n_raw=w.n_raw)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            sp.spmla_indexer_scores(d, dev["iq"][a0:a0 + bn], dev["iw"][a0:a0 + bn], dev["ik"],
+                                    scores_b[:bn])
+            e[1].record()
+            sp.spmla_topk(d, scores_b[:bn], sel[a0:a0 + bn])
+            e[2].record()
+            sp.spmla_sparse_attn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"],
+                                 sel[a0:a0 + bn], out[a0:a0 + bn], lse[a0:a0 + bn])
+            e[3].record()
+            ev["indexer"].append(e)
+    torch.cuda.synchronize()
+    launches = ev["indexer"]
+    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in launches]))
+    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in launches]))
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in launches]))
+
+    bytes_q = attn_bytes_per_query(w)
+    flops_q = attn_flops_per_query(w)
+    attn_bytes_per_launch = float(bytes_q.sum()) / n_bands
+    attn_flops_per_launch = float(flops_q.sum()) / n_bands
+    achieved = attn_bytes_per_launch / (t_attn / 1e3) / 1e9  # GB/s
+    traffic = measured_traffic(w.name)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": "attn_kernel",
+        "bytes_per_launch": attn_bytes_per_launch,
+        "launch_ms": round(t_attn, 4),
+        "mfma_f16_tflops": round(attn_flops_per_launch / (t_attn / 1e3) / 1e12, 1),
+        "mfma_f16_frac": round(attn_flops_per_launch / (t_attn / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+    }
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "n_q": w.n_q,
+            "q_pos0": w.q_pos0,
+            "band": w.band,
+            "top_k": w.top_k,
+            "window": w.window,
+            "ratio": w.ratio,
+            "heads": w.n_heads,
+            "d_qk": w.d_qk,
+            "d_v": w.d_v,
+            "indexer": "int8 4x64",
+        },
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_min": round(float(np.min(per_step)), 4),
+        "wall_s": round(wall, 3),
+        "kernels_ms_per_band": {"indexer": round(t_idx, 4), "topk": round(t_topk, 4),
+                                "attn": round(t_attn, 4)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
