@@ -67,7 +67,8 @@ extern "C" {
  *   d_qk      latent width used by the logits (576 = 512 value + 64 rope).
  *   d_v       value width: the first d_v dims of a latent row (512).
  *   idx_heads, idx_dim   indexer heads and their width (4, 64).
- *   scale     softmax scale applied to the full d_qk-wide dot (1/sqrt(576)).
+ *   scale     softmax scale applied to the full d_qk-wide dot (1/sqrt(576));
+ *             finite and > 0.
  *
  * Kernels cover n_heads == 16, d_qk == 576, d_v == 512, idx_heads == 4,
  * idx_dim == 64, 1 <= top_k <= 4096 and n_comp <= 32768; other valid values

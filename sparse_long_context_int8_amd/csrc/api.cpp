@@ -48,7 +48,8 @@ int check_desc(const spmla_desc* d) {
                 (long long)d->q_pos0 + d->n_q);
   if (d->n_comp != d->n_raw / d->ratio)
     return fail(SPMLA_EINVAL, "n_comp=%d != floor(n_raw/ratio)=%d", d->n_comp, d->n_raw / d->ratio);
-  if (!std::isfinite(d->scale)) return fail(SPMLA_EINVAL, "scale is not finite");
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f))
+    return fail(SPMLA_EINVAL, "scale must be finite and > 0");
   if (d->n_heads != spmla::kHeads || d->d_qk != spmla::kDqk || d->d_v != spmla::kDv)
     return fail(SPMLA_EUNSUPPORTED, "kernels cover n_heads=16, d_qk=576, d_v=512 (got %d, %d, %d)",
                 d->n_heads, d->d_qk, d->d_v);

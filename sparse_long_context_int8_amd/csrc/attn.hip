@@ -7,24 +7,34 @@
 // uses a fast exponential. Here: fp16 operands on matrix cores, fp32
 // accumulation and softmax, exp2 with log2(e) folded into the scale.
 //
-// One workgroup (4 waves) per query token. Its key list is the selected
-// compressed rows followed by the sliding-window raw rows. Keys are streamed
-// in chunks of 64 rows (64 x 1152 B) that are gathered with direct
-// global->LDS loads, so each row crosses the memory system once per query.
+// One workgroup per query token. Its key list is the selected compressed
+// rows followed by the sliding-window raw rows; keys stream through LDS in
+// chunks of CHUNK rows gathered with direct global->LDS loads, so each row
+// crosses the memory system once per query.
 //
-// Per chunk:
-//   wave w: S^T[16 keys x 16 heads] = K[16w..16w+15] . Q^T  (18 MFMA 16x16x32;
-//           K from LDS, Q^T held in registers for the whole query)
-//   all   : exchange S^T through LDS; every wave runs the same online-softmax
-//           update, so each lane owns one head and all of its rescaling is
-//           lane-local
-//   wave w: O^T[128 dims x 16 heads] += V^T . P^T  (16 MFMA; V^T read from
-//           the row-major LDS tile with ds_read_b64_tr_b16 transpose loads,
-//           P^T built in registers from the softmax)
-// LDS rows are stored with a 16-byte-granular XOR swizzle that keeps both the
-// K reads (16 rows x 16 B per pass) and the transposed V reads (8 rows x 32 B
-// per pass) free of bank conflicts.
+// LDS image of a chunk (per buffer):
+//   region A: CHUNK rows x 1024 B = latent dims 0..511 (the value part),
+//             one wave-wide 16-byte-per-lane load per row;
+//   region B: CHUNK rows x 128 B  = latent dims 512..575 (the rope part),
+//             one load per 8 rows.
+// 16-byte units are XOR-swizzled per row so that the K reads (16 rows x 16 B
+// per pass) and the transposed V reads (8 rows x 32 B per pass) hit distinct
+// banks.
+//
+// Per chunk (W waves):
+//   QK: S^T[16 keys x 16 heads] = K . Q^T on v_mfma_f32_16x16x32_f16; the
+//       CHUNK/16 key tiles x (W / tiles) slices of the 576-dim contraction
+//       are spread over the waves, Q^T slices stay in registers;
+//   exchange S^T partials through LDS; every wave runs the same online
+//       softmax update, so each lane owns one head and rescaling is
+//       lane-local;
+//   PV: O^T[512/W dims x 16 heads] += V^T . P^T per wave, V^T fragments read
+//       with ds_read_b64_tr_b16 (the gfx950 transpose load) from the
+//       row-major region A, P^T built in registers.
+// With NBUF == 2 the gather of chunk i+1 is in flight while chunk i computes.
 #include "spmla_internal.h"
+
+#include <type_traits>
 
 namespace spmla {
 namespace {
@@ -33,206 +43,460 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
-
-constexpr int kChunk = 64;                  // keys per chunk
-constexpr int kRowBytes = kDqk * 2;         // 1152
-constexpr int kRowUnits = kRowBytes / 16;   // 72 units of 16 B per row
-constexpr int kKvBytes = kChunk * kRowBytes;
-constexpr int kLoadsPerChunk = kKvBytes / 1024;  // 1 KB per wave-wide load
-constexpr int kLoadsPerWave = kLoadsPerChunk / 4;
-constexpr int kSStride = kChunk + 4;        // floats per head row of the S^T exchange
-static_assert(kLoadsPerChunk % 4 == 0, "chunk must split evenly over 4 waves");
-
-// XOR applied to the low 3 bits of a row's 16-byte unit index.
-__device__ __forceinline__ int swz(int n) {
-  return ((n >> 1) & 1) | ((((n >> 1) ^ (n >> 2)) & 1) << 1) | (((n ^ (n >> 3)) & 1) << 2);
-}
-// Byte offset of 16-byte unit u of LDS row n.
-__device__ __forceinline__ int kv_off(int n, int u) { return n * kRowBytes + ((u ^ swz(n)) << 4); }
-
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(1))) const char gbl_char;
 
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kv[kKvBytes];
-  __shared__ __attribute__((aligned(16))) float sbuf[kHeads * kSStride];
+constexpr int kRowBytes = kDqk * 2;  // 1152: one latent row
+constexpr int kXcds = 8;             // accelerator complex dies, round-robin dispatch
 
-  const int r = blockIdx.x;
+// XOR swizzles of the 16-byte units of the LDS images, as linear maps of
+// the row index bits. They were chosen by measuring the LDS bank-conflict
+// counter on gfx950 for every access pattern of this kernel (K-fragment
+// reads of both key tiles at all 18 k-steps, transposed V reads for every
+// output tile, S^T exchange writes and reads): all of them run without
+// conflicts.
+// Region A (value dims, 64 units per row): bits (n1, n1^n3, n0, n0^n2^n3).
+__device__ __forceinline__ int swz_a(int n) {
+  return ((n >> 1) & 1) | ((((n >> 1) ^ (n >> 3)) & 1) << 1) | ((n & 1) << 2) |
+         (((n ^ (n >> 2) ^ (n >> 3)) & 1) << 3);
+}
+// Region B (rope dims, 8 units per row): bits (n0, n1, n0^n2^n4).
+__device__ __forceinline__ int swz_b(int n) { return (n & 3) | (((n ^ (n >> 2) ^ (n >> 4)) & 1) << 2); }
+// S^T exchange rows (one per head): float4 slot XOR (h1, h0, h2).
+__device__ __forceinline__ int swz_s(int h) { return ((h >> 1) & 1) | ((h & 1) << 1) | (h & 4); }
+
+// Workgroup barrier for LDS traffic. __syncthreads() would also wait for
+// every outstanding global->LDS load (its release fence covers them), i.e.
+// for the gather of the next chunk; those loads are waited for explicitly
+// with vmcnt instead, so this barrier only drains this wave's LDS ops.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]). Emitted as the
+// builtin so the compiler's own wait insertion knows the loads completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// LDS reads of the streamed rows are issued as inline assembly. The
+// compiler's wait insertion would otherwise treat every read of one buffer
+// as possibly depending on the global->LDS loads still landing in the other
+// buffer and wait for all of them (vmcnt(0)), which serializes the gather
+// pipeline. Each group of reads ends with lds_wait() and fence_reg() on the
+// results, so no value is used before it has arrived.
+__device__ __forceinline__ half8 lds_read_b128(unsigned addr) {
+  half8 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ float4v lds_read_f4(unsigned addr) {
+  float4v v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ short4v lds_read_tr16(unsigned addr) {
+  short4v v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ void fence_reg(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+template <int WAVES, int CHUNK, int NBUF, int WPE, bool ROPE_REG>
+struct Cfg {
+  static constexpr int kRowsPerWave = CHUNK / WAVES;
+  static constexpr int kTiles = CHUNK / 16;
+  static constexpr int kHalves = WAVES / kTiles;  // slices of the 576 contraction
+  static constexpr int kSteps = (kDqk / 32) / kHalves;
+  static constexpr int kNt = (kDv / WAVES) / 16;  // 16-dim output tiles per wave
+  static constexpr int kPvSteps = CHUNK / 32;
+  static constexpr int kBLoads = ROPE_REG ? 0 : kRowsPerWave / 8;
+  static constexpr int kBufA = CHUNK * 1024;
+  static constexpr int kBufB = ROPE_REG ? 0 : CHUNK * 128;
+  static constexpr int kBuf = kBufA + kBufB;
+  static constexpr int kSStride = CHUNK;  // floats per head row of S^T partials
+  static constexpr int kSBytes = kHalves * kHeads * kSStride * 4;
+  static constexpr int kLds = NBUF * (kBuf + kSBytes);
+  // k-steps 16 and 17 (the rope dims) belong to the last contraction slice.
+  static constexpr int kRopeSteps = ROPE_REG ? 2 : 0;
+  static_assert(kTiles * kHalves == WAVES, "QK work must split evenly");
+  static_assert((kDqk / 32) % kHalves == 0, "contraction must split evenly");
+  static_assert(ROPE_REG || kRowsPerWave % 8 == 0, "rope loads cover 8 rows");
+  static_assert(kSteps >= kRopeSteps, "rope steps live in one slice");
+  static_assert(CHUNK % 32 == 0, "PV steps are 32 keys");
+  static_assert(kLds * ((WPE * 4) / WAVES) <= 160 * 1024, "LDS for the requested occupancy");
+};
+
+// Softmax reference is moved only when a chunk's max exceeds it by more than
+// this (log2 units); probabilities are then at most 2^8, which fp16 P and
+// fp32 sums hold exactly enough, and the O rescale is skipped for most chunks.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int WAVES, int CHUNK, int NBUF, int WPE, bool ROPE_REG>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_kernel(AttnArgs a) {
+  using C = Cfg<WAVES, CHUNK, NBUF, WPE, ROPE_REG>;
+  __shared__ __attribute__((aligned(1024))) char buf0_[C::kBuf];
+  __shared__ __attribute__((aligned(1024))) char buf1_[NBUF == 2 ? C::kBuf : 16];
+  __shared__ __attribute__((aligned(16))) float sbuf[NBUF * C::kSBytes / 4];
+  lds_char* buf0 = (lds_char*)buf0_;
+  lds_char* buf1 = (lds_char*)buf1_;
+  const unsigned sbuf_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)sbuf;
+
+  // Queries are dealt to the dies in contiguous blocks so that the window
+  // rows shared by neighbouring queries stay in one die's L2.
+  const int per_xcd = (a.n_q + kXcds - 1) / kXcds;
+  const int r = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (r >= a.n_q) return;
+
   const int t = a.q_pos0 + r;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;    // lane group: k-slice of MFMA operands
-  const int c16 = lane & 15;  // MFMA row/column within a 16-wide tile
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
 
   const int nv = min(a.n_comp, (t + 1) / a.ratio);
   const int nsel = min(a.top_k, nv);
   const int ws = max(0, t - a.window + 1);
   const int nk = nsel + (t - ws + 1);
-  const int nchunks = (nk + kChunk - 1) / kChunk;
+  const int nchunks = (nk + CHUNK - 1) / CHUNK;
   const int32_t* sel_row = a.sel + (int64_t)r * a.top_k;
   const char* comp_base = reinterpret_cast<const char*>(a.kv_comp);
   const char* raw_base = reinterpret_cast<const char*>(a.kv_raw);
-  const char* self_row = raw_base + (int64_t)t * kRowBytes;  // always valid
+  const char* self_row = raw_base + (int64_t)t * kRowBytes;
 
-  // Q^T fragments (B operand of S^T = K Q^T): head c16, dims 32s+8g .. +7.
-  half8 qf[kDqk / 32];
-  {
-    const _Float16* qrow = a.q + ((int64_t)r * kHeads + c16) * kDqk + 8 * g;
-#pragma unroll
-    for (int s = 0; s < kDqk / 32; ++s) qf[s] = *reinterpret_cast<const half8*>(qrow + 32 * s);
-  }
+  // QK work item of this wave: key tile and contraction slice.
+  const int tile = wave % C::kTiles;
+  const int half = wave / C::kTiles;
+  const bool has_rope = ROPE_REG && half == C::kHalves - 1;
+  constexpr int kLdsSteps = C::kSteps - C::kRopeSteps;  // steps read from LDS in the last slice
 
-  float4v acc_o[8];
+  half8 qf[C::kSteps];
+  float4v acc_o[C::kNt];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc_o[nt] = float4v{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();  // running max (log2 domain) of head c16
+  for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] = float4v{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -__builtin_inff();  // softmax reference (log2 domain) of head c16
   float l_run = 0.f;                // this lane's share of the softmax sum
 
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int k0 = ch * kChunk;
-    // Row of key k0 + lane (lane-indexed; every wave computes the same).
-    const int key = k0 + lane;
-    const char* kp = self_row;
-    bool ok = false;
+  // Selected index of key k0 + lane: one in-bounds load per call.
+  auto load_sel = [&](int ch) -> int {
+    const int key = min(ch * CHUNK + lane, a.top_k - 1);
+    return __builtin_nontemporal_load(sel_row + key);
+  };
+  // Row pointer and validity of key k0 + lane.
+  auto row_of = [&](int ch, int selv, bool& ok) -> const char* {
+    const int key = ch * CHUNK + lane;
+    ok = false;
+    const char* p = self_row;
     if (key < nsel) {
-      const int s = sel_row[key];
-      ok = (s >= 0) && (s < nv);
-      if (ok) kp = comp_base + (int64_t)s * kRowBytes;
+      ok = (selv >= 0) && (selv < nv);
+      if (ok) p = comp_base + (int64_t)selv * kRowBytes;
     } else if (key < nk) {
       ok = true;
-      kp = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
+      p = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
     }
-    const unsigned long long valid = __ballot(ok);
-    const unsigned kp_lo = (unsigned)(uintptr_t)kp;
-    const unsigned kp_hi = (unsigned)((uintptr_t)kp >> 32);
-
-    // Gather: load q of this wave covers LDS bytes [q*1024, q*1024+1024),
-    // i.e. 16-byte units P = q*64 + lane of the unswizzled row-major image.
+    return p;
+  };
+  // This wave's share of the gather of one chunk, plus (rope in registers)
+  // the rope fragments of the rows this wave scores.
+  const int row0 = wave * C::kRowsPerWave;
+  auto gather = [&](const char* kp, lds_char* buf, half8 (&rope)[2]) {
+    lds_char* bufA = buf;
+    const uintptr_t kpi = (uintptr_t)kp;
+    const unsigned kp_lo = (unsigned)kpi;
+    const unsigned kp_hi = (unsigned)(kpi >> 32);
 #pragma unroll
-    for (int m = 0; m < kLoadsPerWave; ++m) {
-      const int q = wave * kLoadsPerWave + m;
-      const int n0 = (q * 64) / kRowUnits;  // first row touched by this load
-      const int P = q * 64 + lane;
-      const int n = P / kRowUnits;
-      const int p = P - n * kRowUnits;      // physical unit within row n
-      const int u = p ^ swz(n);             // logical unit stored there
-      const unsigned lo0 = __builtin_amdgcn_readlane(kp_lo, n0);
-      const unsigned hi0 = __builtin_amdgcn_readlane(kp_hi, n0);
-      const unsigned lo1 = __builtin_amdgcn_readlane(kp_lo, min(n0 + 1, kChunk - 1));
-      const unsigned hi1 = __builtin_amdgcn_readlane(kp_hi, min(n0 + 1, kChunk - 1));
-      const bool first = (n == n0);
-      const uintptr_t rowp = ((uintptr_t)(first ? hi0 : hi1) << 32) | (first ? lo0 : lo1);
-      const char* src = reinterpret_cast<const char*>(rowp) + (u << 4);
-      __builtin_amdgcn_global_load_lds((gbl_char*)src, (lds_char*)(kv + q * 1024), 16, 0, 0);
+    for (int i = 0; i < C::kRowsPerWave; ++i) {
+      const int n = row0 + i;
+      const unsigned lo = __builtin_amdgcn_readlane(kp_lo, n);
+      const unsigned hi = __builtin_amdgcn_readlane(kp_hi, n);
+      const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
+      const int off = (lane ^ swz_a(n)) << 4;
+      __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), bufA + n * 1024, 16, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // S^T for keys 16*wave .. +15 of this chunk.
-    float4v sacc = float4v{0.f, 0.f, 0.f, 0.f};
-    {
-      const int n = 16 * wave + c16;
+    if constexpr (!ROPE_REG) {
+      lds_char* bufB = bufA + C::kBufA;
 #pragma unroll
-      for (int s = 0; s < kDqk / 32; ++s) {
-        const half8 kf = *reinterpret_cast<const half8*>(kv + kv_off(n, 4 * s + g));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], sacc, 0, 0, 0);
+      for (int j = 0; j < C::kBLoads; ++j) {
+        const int nb = row0 + 8 * j + (lane >> 3);
+        const unsigned lo = __shfl(kp_lo, nb);
+        const unsigned hi = __shfl(kp_hi, nb);
+        const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
+        const int off = (64 + ((lane & 7) ^ swz_b(nb))) << 4;
+        __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), bufB + (row0 + 8 * j) * 128, 16, 0, 0);
+      }
+    } else {
+      if (has_rope) {
+        const int nr = 16 * tile + c16;
+        const unsigned lo = __shfl(kp_lo, nr);
+        const unsigned hi = __shfl(kp_hi, nr);
+        const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
+        rope[0] = *reinterpret_cast<const half8*>(rowp + 1024 + 16 * g);
+        rope[1] = *reinterpret_cast<const half8*>(rowp + 1024 + 64 + 16 * g);
       }
     }
-    // Lane holds S^T[key 16w + 4g + i][head c16]; scale and mask, then share.
-    {
-      float4v z;
+  };
+
+  // Scores, softmax update and PV of one chunk already in `cur`.
+  // With two buffers the S^T exchange area alternates with the chunk buffer,
+  // and no barrier is needed at the end of a chunk: the buffer is refilled
+  // only after the next chunk's barrier, which every wave reaches after its
+  // last read of it.
+  auto compute = [&](lds_char* cur, unsigned long long valid, const half8 (&rope)[2], int sb) {
+    const unsigned bA = (unsigned)(uintptr_t)cur;  // LDS byte address
+    float* sbuf_c = sbuf + sb * (C::kSBytes / 4);
+    const unsigned sbuf_c_addr = sbuf_addr + sb * C::kSBytes;
+    // The contraction slice is a compile-time constant inside qk(), so each
+    // K read address is fixed at compile time (no per-read branches).
+    auto qk = [&](auto half_c) {
+      constexpr int HALF = decltype(half_c)::value;
+      const int n = 16 * tile + c16;
+      half8 kf[C::kSteps];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * wave + 4 * g + i;
-        z[i] = ((valid >> kk) & 1ull) ? sacc[i] * a.scale_log2e : -__builtin_inff();
+      for (int s = 0; s < C::kSteps; ++s) {
+        const int ks = HALF * C::kSteps + s;  // k-step of 32 latent dims
+        if (ks < 16) {
+          kf[s] = lds_read_b128(bA + n * 1024 + (((4 * ks + g) ^ swz_a(n)) << 4));
+        } else if constexpr (!ROPE_REG) {
+          kf[s] = lds_read_b128(bA + C::kBufA + n * 128 + (((4 * (ks - 16) + g) ^ swz_b(n)) << 4));
+        }
       }
-      *reinterpret_cast<float4v*>(&sbuf[c16 * kSStride + 16 * wave + 4 * g]) = z;
+      lds_wait();
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        const int ks = HALF * C::kSteps + s;
+        if (ROPE_REG && ks >= 16) kf[s] = rope[ks - 16];
+        fence_reg(kf[s]);
+      }
+      // Three independent accumulation chains, summed in a fixed order.
+      float4v sacc[3] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s)
+        sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], sacc[s % 3], 0, 0, 0);
+      const float4v ssum = (sacc[0] + sacc[1]) + sacc[2];
+      const int slot = (4 * tile + g) ^ swz_s(c16);
+      *reinterpret_cast<float4v*>(&sbuf_c[(HALF * kHeads + c16) * C::kSStride + 4 * slot]) = ssum;
+    };
+    if (C::kHalves == 1 || half == 0) {
+      qk(std::integral_constant<int, 0>{});
+    } else {
+      qk(std::integral_constant<int, C::kHalves - 1>{});
     }
-    __syncthreads();
+    (void)kLdsSteps;
+    lds_barrier();
 
     // Online softmax for head c16 over keys {32kb + 8g + i}.
-    float zz[2][8];
+    float zz[C::kPvSteps][8];
+    {
+      float4v sp[C::kPvSteps][C::kHalves][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float4v lo = *reinterpret_cast<const float4v*>(&sbuf[c16 * kSStride + 32 * kb + 8 * g]);
-      const float4v hi = *reinterpret_cast<const float4v*>(&sbuf[c16 * kSStride + 32 * kb + 8 * g + 4]);
+      for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        zz[kb][i] = lo[i];
-        zz[kb][4 + i] = hi[i];
-      }
+        for (int hh = 0; hh < C::kHalves; ++hh) {
+          const unsigned srow = sbuf_c_addr + 4u * ((hh * kHeads + c16) * C::kSStride);
+          const int s0 = (8 * kb + 2 * g) ^ swz_s(c16);
+          const int s1 = (8 * kb + 2 * g + 1) ^ swz_s(c16);
+          sp[kb][hh][0] = lds_read_f4(srow + 16u * s0);
+          sp[kb][hh][1] = lds_read_f4(srow + 16u * s1);
+        }
+      lds_wait();
+#pragma unroll
+      for (int kb = 0; kb < C::kPvSteps; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < C::kHalves; ++hh) {
+          fence_reg(sp[kb][hh][0]);
+          fence_reg(sp[kb][hh][1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            zz[kb][i] = hh == 0 ? sp[kb][hh][0][i] : zz[kb][i] + sp[kb][hh][0][i];
+            zz[kb][4 + i] = hh == 0 ? sp[kb][hh][1][i] : zz[kb][4 + i] + sp[kb][hh][1][i];
+          }
+        }
+    }
+    // Keys past the end of the list (or rejected indices) only occur in
+    // chunks that are not entirely valid.
+    constexpr unsigned long long kChunkMask = CHUNK == 64 ? ~0ull : ((1ull << CHUNK) - 1);
+    if ((valid & kChunkMask) != kChunkMask) {
+#pragma unroll
+      for (int kb = 0; kb < C::kPvSteps; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kk = 32 * kb + 8 * g + i;
+          if (!((valid >> kk) & 1ull)) zz[kb][i] = -__builtin_inff();
+        }
     }
     float cmax = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) cmax = fmaxf(cmax, zz[kb][i]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    half8 pf[2];
+    cmax *= a.scale_log2e;  // scale > 0, so the max commutes with it
+    // Move the reference (and rescale O and l) only when needed; the test is
+    // made per head and the branch is taken if any head needs it.
+    const bool move = cmax > m_ref + kRescaleThreshold;
+    if (__ballot(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - cmax) : 1.f;
+      if (move) m_ref = cmax;
+      l_run *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] *= alpha;
+    }
+    const float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+    half8 pf[C::kPvSteps];
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(zz[kb][i] - m_use);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zz[kb][i], a.scale_log2e, -m_use));
         psum += p;
         pf[kb][i] = (_Float16)p;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc_o[nt] *= alpha;
+    l_run += psum;
 
-    // O^T[dims 128w + 16nt + 4g + i][head c16] += V^T . P^T
-    {
-      const int tri = (lane >> 2) & 3;  // row within the 4-row transpose block
-      const int trc = lane & 3;         // 4-column slice within 16 columns
+    // O^T[dims (512/W) wave + 16nt + 4g + i][head c16] += V^T . P^T
+    const int tri = (lane >> 2) & 3;
+    const int trc = lane & 3;
+    constexpr int kPvGroup = C::kNt * C::kPvSteps > 4 ? (4 / C::kPvSteps > 0 ? 4 / C::kPvSteps : 1) : C::kNt;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int dv0 = 128 * wave + 16 * nt;
+    for (int nt0 = 0; nt0 < C::kNt; nt0 += kPvGroup) {
+      short4v vt[kPvGroup][C::kPvSteps][2];
+#pragma unroll
+      for (int j = 0; j < kPvGroup; ++j) {
+        const int dv0 = (kDv / WAVES) * wave + 16 * (nt0 + j);
         const int unit = (dv0 >> 3) + (trc >> 1);
         const int sub = (trc & 1) << 3;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < C::kPvSteps; ++kb) {
           const int n_lo = 32 * kb + 8 * g + tri;
           const int n_hi = n_lo + 4;
-          const short4v vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(kv + kv_off(n_lo, unit) + sub));
-          const short4v vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(kv + kv_off(n_hi, unit) + sub));
-          const half4 hlo = __builtin_bit_cast(half4, vlo);
-          const half4 hhi = __builtin_bit_cast(half4, vhi);
-          const half8 vf = half8{hlo[0], hlo[1], hlo[2], hlo[3], hhi[0], hhi[1], hhi[2], hhi[3]};
-          acc_o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[kb], acc_o[nt], 0, 0, 0);
+          vt[j][kb][0] = lds_read_tr16(bA + n_lo * 1024 + ((unit ^ swz_a(n_lo)) << 4) + sub);
+          vt[j][kb][1] = lds_read_tr16(bA + n_hi * 1024 + ((unit ^ swz_a(n_hi)) << 4) + sub);
         }
       }
+      lds_wait();
+#pragma unroll
+      for (int j = 0; j < kPvGroup; ++j)
+#pragma unroll
+        for (int kb = 0; kb < C::kPvSteps; ++kb) {
+          fence_reg(vt[j][kb][0]);
+          fence_reg(vt[j][kb][1]);
+          const half4 hlo = __builtin_bit_cast(half4, vt[j][kb][0]);
+          const half4 hhi = __builtin_bit_cast(half4, vt[j][kb][1]);
+          const half8 vf = half8{hlo[0], hlo[1], hlo[2], hlo[3], hhi[0], hhi[1], hhi[2], hhi[3]};
+          acc_o[nt0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[kb], acc_o[nt0 + j], 0, 0, 0);
+        }
     }
-    __syncthreads();  // kv and sbuf are overwritten by the next chunk
+    if constexpr (NBUF == 1) lds_barrier();  // `cur` and sbuf are refilled next
+  };
+
+  // Prologue: start the gather of chunk 0, then load Q^T while it flies.
+  unsigned long long valid_cur;
+  half8 rope_cur[2], rope_nxt[2];
+  {
+    const int sel0 = load_sel(0);
+    bool ok0;
+    const char* kp0 = row_of(0, sel0, ok0);
+    valid_cur = __ballot(ok0);
+    gather(kp0, buf0, rope_cur);
+  }
+  {
+    const _Float16* qrow = a.q + ((int64_t)r * kHeads + c16) * kDqk + 8 * g;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s)
+      qf[s] = *reinterpret_cast<const half8*>(qrow + 32 * (half * C::kSteps + s));
+  }
+  int sel_next = load_sel(min(1, nchunks - 1));
+
+  if constexpr (NBUF == 2) {
+    // Chunk ch computes from `cur` while the gather of chunk ch+1 lands in
+    // `nxt`. The only wait is for this chunk's gather (and everything issued
+    // before it), right before the barrier that publishes it.
+    auto step = [&](int ch, lds_char* cur, lds_char* nxt) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      unsigned long long valid_next = 0;
+      if (ch + 1 < nchunks) {
+        bool okn;
+        const char* kpn = row_of(ch + 1, sel_next, okn);
+        valid_next = __ballot(okn);
+        sel_next = load_sel(min(ch + 2, nchunks - 1));
+        gather(kpn, nxt, rope_nxt);
+      }
+      compute(cur, valid_cur, rope_cur, ch & 1);
+      valid_cur = valid_next;
+      rope_cur[0] = rope_nxt[0];
+      rope_cur[1] = rope_nxt[1];
+    };
+    for (int ch = 0;;) {
+      step(ch, buf0, buf1);
+      if (++ch >= nchunks) break;
+      step(ch, buf1, buf0);
+      if (++ch >= nchunks) break;
+    }
+  } else {
+    for (int ch = 0; ch < nchunks; ++ch) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      compute(buf0, valid_cur, rope_cur, 0);
+      if (ch + 1 < nchunks) {
+        bool okn;
+        const char* kpn = row_of(ch + 1, sel_next, okn);
+        valid_cur = __ballot(okn);
+        sel_next = load_sel(min(ch + 2, nchunks - 1));
+        gather(kpn, buf0, rope_cur);
+      }
+    }
   }
 
-  // Finish: total softmax sum of head c16 (same value in its 4 lanes).
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot = l_tot + __shfl_xor(l_tot, 32);
   const float inv = 1.0f / l_tot;
-  float* orow = a.out + ((int64_t)r * kHeads + c16) * kDv + 128 * wave + 4 * g;
+  float* orow = a.out + ((int64_t)r * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    *reinterpret_cast<float4v*>(orow + 16 * nt) = acc_o[nt] * inv;
+  for (int nt = 0; nt < C::kNt; ++nt) {
+    const float4v v = acc_o[nt] * inv;
+    __builtin_nontemporal_store(v, reinterpret_cast<float4v*>(orow + 16 * nt));
   }
   if (a.lse && wave == 0 && g == 0) {
-    a.lse[(int64_t)r * kHeads + c16] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    a.lse[(int64_t)r * kHeads + c16] = (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
+
+#ifndef SPMLA_ATTN_WAVES
+#define SPMLA_ATTN_WAVES 4
+#endif
+#ifndef SPMLA_ATTN_CHUNK
+#define SPMLA_ATTN_CHUNK 32
+#endif
+#ifndef SPMLA_ATTN_NBUF
+#define SPMLA_ATTN_NBUF 2
+#endif
+#ifndef SPMLA_ATTN_WPE
+#define SPMLA_ATTN_WPE 2
+#endif
+#ifndef SPMLA_ATTN_ROPE_REG
+#define SPMLA_ATTN_ROPE_REG 0
+#endif
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.n_q <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_kernel, dim3(a.n_q), dim3(256), 0, stream, a);
+  const int per_xcd = (a.n_q + kXcds - 1) / kXcds;
+  constexpr int W = SPMLA_ATTN_WAVES;
+  hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE,
+                                  (bool)SPMLA_ATTN_ROPE_REG>),
+                     dim3(per_xcd * kXcds), dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -68,6 +68,8 @@ BAD = [
     (dict(n_comp=63), sp.SPMLA_EINVAL, "n_comp"),
     (dict(d_v=600), sp.SPMLA_EINVAL, "d_v"),
     (dict(scale=float("nan")), sp.SPMLA_EINVAL, "scale"),
+    (dict(scale=0.0), sp.SPMLA_EINVAL, "scale"),
+    (dict(scale=-0.5), sp.SPMLA_EINVAL, "scale"),
     (dict(n_heads=8), sp.SPMLA_EUNSUPPORTED, "n_heads"),
     (dict(d_qk=512, d_v=512), sp.SPMLA_EUNSUPPORTED, "d_qk"),
     (dict(idx_dim=32), sp.SPMLA_EUNSUPPORTED, "idx_dim"),
