@@ -114,7 +114,14 @@ struct Cfg {
   static constexpr int kRowsPerWave = CHUNK / WAVES;
   static constexpr int kTiles = CHUNK / 16;
   static constexpr int kHalves = WAVES / kTiles;  // slices of the 576 contraction
-  static constexpr int kSteps = (kDqk / 32) / kHalves;
+  // Slice h covers k-steps [start(h), start(h) + len(h)) of the 18 steps of
+  // 32 latent dims; slices differ in length by at most one step.
+  static constexpr int kAllSteps = kDqk / 32;
+  static constexpr int kSteps = (kAllSteps + kHalves - 1) / kHalves;  // longest slice
+  static constexpr int len(int h) { return kAllSteps / kHalves + (h < kAllSteps % kHalves ? 1 : 0); }
+  static constexpr int start(int h) {
+    return h * (kAllSteps / kHalves) + (h < kAllSteps % kHalves ? h : kAllSteps % kHalves);
+  }
   static constexpr int kNt = (kDv / WAVES) / 16;  // 16-dim output tiles per wave
   static constexpr int kPvSteps = CHUNK / 32;
   static constexpr int kBLoads = ROPE_REG ? 0 : kRowsPerWave / 8;
@@ -125,11 +132,9 @@ struct Cfg {
   static constexpr int kSBytes = kHalves * kHeads * kSStride * 4;
   static constexpr int kLds = NBUF * (kBuf + kSBytes);
   // k-steps 16 and 17 (the rope dims) belong to the last contraction slice.
-  static constexpr int kRopeSteps = ROPE_REG ? 2 : 0;
   static_assert(kTiles * kHalves == WAVES, "QK work must split evenly");
-  static_assert((kDqk / 32) % kHalves == 0, "contraction must split evenly");
   static_assert(ROPE_REG || kRowsPerWave % 8 == 0, "rope loads cover 8 rows");
-  static_assert(kSteps >= kRopeSteps, "rope steps live in one slice");
+  static_assert(start(kHalves - 1) <= 16, "rope steps live in the last slice");
   static_assert(CHUNK % 32 == 0, "PV steps are 32 keys");
   static_assert(kLds * ((WPE * 4) / WAVES) <= 160 * 1024, "LDS for the requested occupancy");
 };
@@ -176,7 +181,6 @@ void attn_kernel(AttnArgs a) {
   const int tile = wave % C::kTiles;
   const int half = wave / C::kTiles;
   const bool has_rope = ROPE_REG && half == C::kHalves - 1;
-  constexpr int kLdsSteps = C::kSteps - C::kRopeSteps;  // steps read from LDS in the last slice
 
   half8 qf[C::kSteps];
   float4v acc_o[C::kNt];
@@ -258,10 +262,12 @@ void attn_kernel(AttnArgs a) {
     auto qk = [&](auto half_c) {
       constexpr int HALF = decltype(half_c)::value;
       const int n = 16 * tile + c16;
+      constexpr int kLen = C::len(HALF);
+      constexpr int kStart = C::start(HALF);
       half8 kf[C::kSteps];
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        const int ks = HALF * C::kSteps + s;  // k-step of 32 latent dims
+      for (int s = 0; s < kLen; ++s) {
+        const int ks = kStart + s;  // k-step of 32 latent dims
         if (ks < 16) {
           kf[s] = lds_read_b128(bA + n * 1024 + (((4 * ks + g) ^ swz_a(n)) << 4));
         } else if constexpr (!ROPE_REG) {
@@ -270,26 +276,30 @@ void attn_kernel(AttnArgs a) {
       }
       lds_wait();
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        const int ks = HALF * C::kSteps + s;
+      for (int s = 0; s < kLen; ++s) {
+        const int ks = kStart + s;
         if (ROPE_REG && ks >= 16) kf[s] = rope[ks - 16];
         fence_reg(kf[s]);
       }
       // Three independent accumulation chains, summed in a fixed order.
       float4v sacc[3] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s)
+      for (int s = 0; s < kLen; ++s)
         sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], sacc[s % 3], 0, 0, 0);
       const float4v ssum = (sacc[0] + sacc[1]) + sacc[2];
       const int slot = (4 * tile + g) ^ swz_s(c16);
       *reinterpret_cast<float4v*>(&sbuf_c[(HALF * kHeads + c16) * C::kSStride + 4 * slot]) = ssum;
     };
-    if (C::kHalves == 1 || half == 0) {
+    if (half == 0) {
       qk(std::integral_constant<int, 0>{});
-    } else {
-      qk(std::integral_constant<int, C::kHalves - 1>{});
+    } else if constexpr (C::kHalves == 2) {
+      qk(std::integral_constant<int, 1>{});
+    } else if constexpr (C::kHalves == 4) {
+      if (half == 1) qk(std::integral_constant<int, 1>{});
+      else if (half == 2) qk(std::integral_constant<int, 2>{});
+      else qk(std::integral_constant<int, 3>{});
     }
-    (void)kLdsSteps;
+    static_assert(C::kHalves == 1 || C::kHalves == 2 || C::kHalves == 4, "slice dispatch");
     lds_barrier();
 
     // Online softmax for head c16 over keys {32kb + 8g + i}.
@@ -411,9 +421,10 @@ void attn_kernel(AttnArgs a) {
   }
   {
     const _Float16* qrow = a.q + ((int64_t)r * kHeads + c16) * kDqk + 8 * g;
+    const int q_start = C::start(half), q_len = C::len(half);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
-      qf[s] = *reinterpret_cast<const half8*>(qrow + 32 * (half * C::kSteps + s));
+      if (s < q_len) qf[s] = *reinterpret_cast<const half8*>(qrow + 32 * (q_start + s));
   }
   int sel_next = load_sel(min(1, nchunks - 1));
 
