@@ -78,9 +78,12 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Row stride of the band score matrix in the prefill workspace: a multiple
+// of 4 so that the indexer writes 16-byte groups.
+int64_t band_ld(const spmla_desc* d) { return ((int64_t)d->n_comp + 3) / 4 * 4; }
 size_t scores_bytes_per_band(const spmla_desc* d) {
   const int64_t rows = d->band < d->n_q ? d->band : d->n_q;
-  return (size_t)rows * (size_t)d->n_comp * sizeof(int32_t);
+  return (size_t)rows * (size_t)band_ld(d) * sizeof(int32_t);
 }
 size_t sel_bytes_per_band(const spmla_desc* d) {
   const int64_t rows = d->band < d->n_q ? d->band : d->n_q;
@@ -149,6 +152,8 @@ int spmla_indexer_scores(const spmla_desc* d, const int8_t* iq, const int8_t* iw
   a.q_pos0 = d->q_pos0;
   a.n_comp = d->n_comp;
   a.ratio = d->ratio;
+  a.fill_invisible = 1;  // the full matrix is the documented output
+  a.span = 0;
   return hip_status(spmla::launch_indexer(a, (hipStream_t)stream), "indexer launch");
 }
 
@@ -237,17 +242,19 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       ia.iw = iw + b0 * spmla::kIdxHeads;
       ia.ik = ik;
       ia.scores = band_scores;
-      ia.ld_scores = d->n_comp;
+      ia.ld_scores = band_ld(d);
       ia.n_q = bn;
       ia.q_pos0 = pos0;
       ia.n_comp = d->n_comp;
       ia.ratio = d->ratio;
+      ia.fill_invisible = 0;  // top-k reads only the rows each token can see
+      ia.span = 0;
       rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
       if (rc) return rc;
     }
     spmla::TopkArgs ta;
     ta.scores = band_scores;
-    ta.ld_scores = d->n_comp;
+    ta.ld_scores = band_ld(d);
     ta.sel = sel;
     ta.n_sel = nullptr;
     ta.n_q = bn;

@@ -30,6 +30,8 @@ struct IndexerArgs {
   int32_t q_pos0;     // absolute position of query 0 of this launch
   int32_t n_comp;
   int32_t ratio;
+  int32_t fill_invisible;  // also write INT32_MIN where no token can see the row
+  int32_t span;            // compressed rows per workgroup (set by the launcher)
 };
 
 struct TopkArgs {
