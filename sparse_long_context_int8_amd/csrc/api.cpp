@@ -90,6 +90,14 @@ size_t sel_bytes_per_band(const spmla_desc* d) {
   return (size_t)rows * (size_t)d->top_k * sizeof(int32_t);
 }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+// Per-band scratch: the score band of the dense selection or the fused
+// selection's thresholds, slot counts and candidates, whichever is larger.
+size_t band_scratch_bytes(const spmla_desc* d) {
+  const int rows = d->band < d->n_q ? d->band : d->n_q;
+  const size_t dense = round_up(scores_bytes_per_band(d), 256);
+  const size_t fused = spmla::fused_workspace_bytes(rows, spmla::fused_plan(d->n_comp, d->top_k));
+  return dense > fused ? dense : fused;
+}
 
 spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
                           const uint16_t* kv_raw, const int32_t* sel, float* out, float* lse) {
@@ -198,7 +206,7 @@ int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (!bytes) return fail(SPMLA_EINVAL, "bytes is NULL");
-  *bytes = round_up(scores_bytes_per_band(d), 256) + round_up(sel_bytes_per_band(d), 256);
+  *bytes = band_scratch_bytes(d) + round_up(sel_bytes_per_band(d), 256);
   return ok();
 }
 
@@ -229,41 +237,60 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
   hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   int32_t* band_scores = reinterpret_cast<int32_t*>(ws);
-  int32_t* band_sel = reinterpret_cast<int32_t*>(ws + round_up(scores_bytes_per_band(d), 256));
+  int32_t* band_sel = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d));
 
   for (int64_t b0 = 0; b0 < d->n_q; b0 += d->band) {
     const int bn = (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band);
     const int pos0 = d->q_pos0 + (int)b0;
     int32_t* sel = sel_out ? sel_out + b0 * d->top_k : band_sel;
 
-    if (d->n_comp > 0) {
-      spmla::IndexerArgs ia;
-      ia.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
-      ia.iw = iw + b0 * spmla::kIdxHeads;
-      ia.ik = ik;
-      ia.scores = band_scores;
-      ia.ld_scores = band_ld(d);
-      ia.n_q = bn;
-      ia.q_pos0 = pos0;
-      ia.n_comp = d->n_comp;
-      ia.ratio = d->ratio;
-      ia.fill_invisible = 0;  // top-k reads only the rows each token can see
-      ia.span = 0;
-      rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
+    if (d->n_comp > 0 && spmla::fused_applies(bn, pos0, d->n_comp, d->ratio, d->top_k)) {
+      // Long history: indexer -> top-k handoff without the score band.
+      spmla::FusedArgs fa{};
+      fa.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
+      fa.iw = iw + b0 * spmla::kIdxHeads;
+      fa.ik = ik;
+      fa.sel = sel;
+      fa.n_sel = nullptr;
+      fa.n_q = bn;
+      fa.q_pos0 = pos0;
+      fa.n_comp = d->n_comp;
+      fa.ratio = d->ratio;
+      fa.top_k = d->top_k;
+      fa.plan = spmla::fused_plan(d->n_comp, d->top_k);
+      spmla::fused_bind_workspace(fa, ws);
+      rc = hip_status(spmla::launch_fused_topk(fa, st), "fused selection launch");
+      if (rc) return rc;
+    } else {
+      if (d->n_comp > 0) {
+        spmla::IndexerArgs ia;
+        ia.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
+        ia.iw = iw + b0 * spmla::kIdxHeads;
+        ia.ik = ik;
+        ia.scores = band_scores;
+        ia.ld_scores = band_ld(d);
+        ia.n_q = bn;
+        ia.q_pos0 = pos0;
+        ia.n_comp = d->n_comp;
+        ia.ratio = d->ratio;
+        ia.fill_invisible = 0;  // top-k reads only the rows each token can see
+        ia.span = 0;
+        rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
+        if (rc) return rc;
+      }
+      spmla::TopkArgs ta;
+      ta.scores = band_scores;
+      ta.ld_scores = band_ld(d);
+      ta.sel = sel;
+      ta.n_sel = nullptr;
+      ta.n_q = bn;
+      ta.q_pos0 = pos0;
+      ta.n_comp = d->n_comp;
+      ta.ratio = d->ratio;
+      ta.top_k = d->top_k;
+      rc = hip_status(spmla::launch_topk(ta, st), "top-k launch");
       if (rc) return rc;
     }
-    spmla::TopkArgs ta;
-    ta.scores = band_scores;
-    ta.ld_scores = band_ld(d);
-    ta.sel = sel;
-    ta.n_sel = nullptr;
-    ta.n_q = bn;
-    ta.q_pos0 = pos0;
-    ta.n_comp = d->n_comp;
-    ta.ratio = d->ratio;
-    ta.top_k = d->top_k;
-    rc = hip_status(spmla::launch_topk(ta, st), "top-k launch");
-    if (rc) return rc;
 
     spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
                                    out + b0 * spmla::kHeads * spmla::kDv,

@@ -28,6 +28,62 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kQTile = 64;  // query tokens per workgroup (16 per wave)
 constexpr int kJStep = 64;  // compressed rows per step (4 MFMA column tiles)
 
+// The 64 tokens of a workgroup seen from one lane: A tiles (tile m holds
+// tokens t_base + 4m .. +3 of the wave), and the token whose scores this lane
+// receives in each tile, with its weights and visible-row count.
+struct TokenTiles {
+  v4i afrag[4];
+  int wpack[4];  // 4 x int8 weights of the lane's token in tile m
+  int tok[4];
+  int nv[4];
+
+  __device__ __forceinline__ void load(const int8_t* iq, const int8_t* iw, int n_q, int q_pos0, int n_comp,
+                                       int ratio, int t_base, int col, int grp) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // Row r of tile m is the 64-byte vector iq[t_base + 4m + r/4][r%4][:].
+      const int row = 4 * (t_base + 4 * m) + col;
+      const int tok_a = t_base + 4 * m + (col >> 2);
+      afrag[m] = tok_a < n_q ? *reinterpret_cast<const v4i*>(iq + (int64_t)row * kIdxDim + grp * 16)
+                             : v4i{0, 0, 0, 0};
+      tok[m] = t_base + 4 * m + grp;
+      wpack[m] = tok[m] < n_q ? *reinterpret_cast<const int*>(iw + (int64_t)tok[m] * kIdxHeads) : 0;
+      nv[m] = min(n_comp, (q_pos0 + tok[m] + 1) / ratio);
+    }
+  }
+};
+
+// B tiles of one 64-row step: tile u, column c holds compressed row j0+4c+u.
+__device__ __forceinline__ void load_b(const int8_t* ik, int n_comp, int j0, int col, int grp, v4i (&b)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jr = j0 + 4 * col + u;
+    b[u] = jr < n_comp ? *reinterpret_cast<const v4i*>(ik + (int64_t)jr * kIdxDim + grp * 16) : v4i{0, 0, 0, 0};
+  }
+}
+
+// Weighted head sum of one 16x16 result: the 4 heads of the lane's token.
+__device__ __forceinline__ int head_sum(v4i acc, int wpack) {
+  int v = 0;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int wh = (int)(int8_t)((wpack >> (8 * h)) & 0xff);
+    v += wh * max(acc[h], 0);
+  }
+  return v;
+}
+
+// Scores of the lane's token in tile m for rows j0+4c .. j0+4c+3.
+__device__ __forceinline__ v4i tile_scores(const TokenTiles& tt, int m, const v4i (&b)[4]) {
+  v4i s;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt.afrag[m], b[u], v4i{0, 0, 0, 0}, 0, 0, 0);
+    s[u] = head_sum(acc, tt.wpack[m]);
+  }
+  return s;
+}
+
 // VEC: 16-byte stores; the row stride is a multiple of 4 and at least n_comp
 // rounded up to 4, so a group that straddles n_comp stays inside the row
 // (its entries past n_comp are INT32_MIN).
@@ -46,24 +102,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerArgs a) {
 
   const int col = lane & 15;  // MFMA column within a 16-wide tile
   const int grp = lane >> 4;  // which 16-byte slice of the 64-wide k dim
-
-  // A fragments: 4 tiles of 4 tokens x 4 heads. Row r of tile m is the
-  // 64-byte vector iq[t_base + 4m + r/4][r%4][:], i.e. flat row 4*t + r.
-  v4i afrag[4];
-  int wpack[4];  // weights of the token this lane owns in tile m (4 x int8)
-  int tok_of[4];
-  int nv_of[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int row = 4 * (t_base + 4 * m) + col;
-    const int tok_a = t_base + 4 * m + (col >> 2);
-    afrag[m] = tok_a < a.n_q ? *reinterpret_cast<const v4i*>(a.iq + (int64_t)row * kIdxDim + grp * 16)
-                             : v4i{0, 0, 0, 0};
-    const int tok = t_base + 4 * m + grp;
-    tok_of[m] = tok;
-    wpack[m] = tok < a.n_q ? *reinterpret_cast<const int*>(a.iw + (int64_t)tok * kIdxHeads) : 0;
-    nv_of[m] = min(a.n_comp, (a.q_pos0 + tok + 1) / a.ratio);
-  }
+  TokenTiles tt;
+  tt.load(a.iq, a.iw, a.n_q, a.q_pos0, a.n_comp, a.ratio, t_base, col, grp);
 
   auto store4 = [&](int tok, int j, v4i s) {
     int32_t* dst = a.scores + (int64_t)tok * a.ld_scores + j;
@@ -80,32 +120,16 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerArgs a) {
   int j0 = j_begin;
   for (; j0 < j_score_end; j0 += kJStep) {
     v4i bfrag[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int jr = j0 + 4 * col + u;
-      bfrag[u] = jr < a.n_comp ? *reinterpret_cast<const v4i*>(a.ik + (int64_t)jr * kIdxDim + grp * 16)
-                               : v4i{0, 0, 0, 0};
-    }
+    load_b(a.ik, a.n_comp, j0, col, grp, bfrag);
     const int jl = j0 + 4 * col;  // first of this lane's 4 rows
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      v4i acc[4];
+      v4i s = tile_scores(tt, m, bfrag);
+      if (tt.tok[m] >= a.n_q) continue;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        acc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag[m], bfrag[u], v4i{0, 0, 0, 0}, 0, 0, 0);
-      if (tok_of[m] >= a.n_q) continue;
-      v4i s;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int v = 0;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int wh = (int)(int8_t)((wpack[m] >> (8 * h)) & 0xff);
-          v += wh * max(acc[u][h], 0);
-        }
-        s[u] = jl + u < nv_of[m] ? v : INT32_MIN;
-      }
-      if (jl < j_end) store4(tok_of[m], jl, s);
+        if (jl + u >= tt.nv[m]) s[u] = INT32_MIN;
+      if (jl < j_end) store4(tt.tok[m], jl, s);
     }
   }
   // Rows no token of this wave can see.
@@ -115,9 +139,190 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerArgs a) {
       const int jl = j0 + 4 * col;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        if (tok_of[m] < a.n_q && jl < j_end) store4(tok_of[m], jl, inv);
+        if (tt.tok[m] < a.n_q && jl < j_end) store4(tt.tok[m], jl, inv);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fused selection, score-side passes.
+
+// Monotone 11-bit code of an int32 score: 32 exact small magnitudes, then
+// 32 steps per power of two (a float with 5 mantissa bits), negatives
+// mirrored below 1024. code(x) <= code(y) whenever x <= y.
+__device__ __forceinline__ int mag_code(unsigned y) {  // 0 .. 863
+  if (y < 32) return (int)y;
+  const int e = 31 - __clz((int)y);
+  return 32 + 32 * (e - 5) + (int)((y >> (e - 5)) & 31);
+}
+__device__ __forceinline__ int score_code(int x) {
+  return x >= 0 ? 1024 + mag_code((unsigned)x) : 1023 - mag_code((unsigned)(-(x + 1)));
+}
+// Smallest magnitude with a given code (0 .. 864; 864 gives 2^31).
+__device__ __forceinline__ int64_t mag_lo(int f) {
+  if (f < 32) return f;
+  const int e = (f - 32) / 32 + 5;
+  return (int64_t)(32 + (f - 32) % 32) << (e - 5);
+}
+// Smallest score whose code is c: every score >= it has code >= c.
+__device__ __forceinline__ int code_lo(int c) {
+  return c >= 1024 ? (int)mag_lo(c - 1024) : (int)(-mag_lo(1023 - c + 1));
+}
+
+constexpr int kCodes = 2048;
+
+// Threshold pass (also clears the recompute list of the finish pass): one
+// workgroup per 4 tokens (one A tile); its 4 waves take
+// turns over 16-row steps of the sampled rows j = stride * i. Each sampled
+// visible score lands in a per-token LDS histogram of score codes; the
+// threshold is the lowest score of the code bin in which the count from the
+// top reaches `rank` (INT32_MIN if fewer samples than that).
+__global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
+  __shared__ int hist[4][kCodes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int t0 = blockIdx.x * 4;
+  for (int i = threadIdx.x; i < 4 * kCodes; i += 256) (&hist[0][0])[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_redo = 0;  // the finish pass fills the list
+
+  const int tok_a = t0 + (col >> 2);
+  const v4i afrag = tok_a < a.n_q
+                        ? *reinterpret_cast<const v4i*>(a.iq + ((int64_t)4 * t0 + col) * kIdxDim + grp * 16)
+                        : v4i{0, 0, 0, 0};
+  const int tok = t0 + grp;
+  const int wpack = tok < a.n_q ? *reinterpret_cast<const int*>(a.iw + (int64_t)tok * kIdxHeads) : 0;
+  const int nv = tok < a.n_q ? min(a.n_comp, (a.q_pos0 + tok + 1) / a.ratio) : 0;
+  const int t_last = min(t0 + 3, a.n_q - 1);
+  const int nv_max = min(a.n_comp, (a.q_pos0 + t_last + 1) / a.ratio);
+  const int stride = a.plan.stride;
+  const int n_steps = (nv_max + 16 * stride - 1) / (16 * stride);
+  __syncthreads();
+
+  constexpr int kUnroll = 4;
+  for (int s0 = wave * kUnroll; s0 < n_steps; s0 += 4 * kUnroll) {
+    v4i b[kUnroll];
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+      const int j = stride * (16 * (s0 + q) + col);
+      b[q] = (s0 + q < n_steps && j < a.n_comp)
+                 ? *reinterpret_cast<const v4i*>(a.ik + (int64_t)j * kIdxDim + grp * 16)
+                 : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+      const int j = stride * (16 * (s0 + q) + col);
+      const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, b[q], v4i{0, 0, 0, 0}, 0, 0, 0);
+      if (s0 + q < n_steps && j < nv) atomicAdd(&hist[grp][score_code(head_sum(acc, wpack))], 1);
+    }
+  }
+  __syncthreads();
+
+  // Wave w sets the threshold of token t0 + w; lane l owns codes
+  // kCodes-1 - kPer*l down to kCodes - kPer*(l+1) (scanned from the top).
+  constexpr int kPer = kCodes / 64;
+  const int tw = t0 + wave;
+  if (tw >= a.n_q) return;
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) tot += hist[wave][kCodes - 1 - kPer * lane - i];
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  const int total = __shfl(incl, 63);
+  const int need = a.plan.rank;
+  int code = -1;
+  int above = incl - tot;
+  if (above < need && need <= incl) {
+    for (int i = 0; i < kPer; ++i) {
+      const int c = kCodes - 1 - kPer * lane - i;
+      above += hist[wave][c];
+      if (above >= need) {
+        code = c;
+        break;
+      }
+    }
+  }
+  // One lane found it (or none, when the sample is smaller than the rank).
+  const unsigned long long found = __ballot(code >= 0);
+  if (found == 0) {
+    if (lane == 0) a.thresh[tw] = INT32_MIN;
+  } else if (code >= 0) {
+    a.thresh[tw] = code_lo(code);
+  }
+  (void)total;
+}
+
+// Collect pass: the indexer's 64-token x span tiling with exact scores; every
+// visible score >= the token's threshold is written as (score, row) into the
+// token's slots for this span, in row order. The 16 lanes holding one token
+// in a tile assign slots with a prefix sum; the slot count written at the end
+// is the true count, so the finish pass can detect a full span.
+__global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t_base = blockIdx.y * kQTile + wave * 16;
+  if (t_base >= a.n_q) return;
+  const int span_idx = blockIdx.x;
+  const int j_begin = span_idx * a.plan.span;
+  const int j_end = min(a.n_comp, j_begin + a.plan.span);
+  const int t_last = min(t_base + 15, a.n_q - 1);
+  const int nv_wave = min(a.n_comp, (a.q_pos0 + t_last + 1) / a.ratio);
+  const int col = lane & 15, grp = lane >> 4;
+  const int cap = a.plan.cap;
+
+  TokenTiles tt;
+  tt.load(a.iq, a.iw, a.n_q, a.q_pos0, a.n_comp, a.ratio, t_base, col, grp);
+  int thr[4], run[4];
+  int32_t* slots[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bool ok = tt.tok[m] < a.n_q;
+    thr[m] = ok ? a.thresh[tt.tok[m]] : INT32_MAX;
+    run[m] = 0;
+    slots[m] = a.cand + 2 * (((int64_t)(ok ? tt.tok[m] : 0) * a.plan.n_spans + span_idx) * cap);
+  }
+
+  const int j_score_end = min(j_end, nv_wave);
+  for (int j0 = j_begin; j0 < j_score_end; j0 += kJStep) {
+    v4i bfrag[4];
+    load_b(a.ik, a.n_comp, j0, col, grp, bfrag);
+    const int jl = j0 + 4 * col;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const v4i s = tile_scores(tt, m, bfrag);
+      bool pass[4];
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pass[u] = tt.tok[m] < a.n_q && jl + u < tt.nv[m] && jl + u < j_end && s[u] >= thr[m];
+        c += pass[u] ? 1 : 0;
+      }
+      // Inclusive prefix over the 16 lanes of this token.
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const int y = __shfl_up(incl, o, 16);
+        if (col >= o) incl += y;
+      }
+      const int tot = __shfl(incl, 15, 16);
+      int pos = run[m] + incl - c;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pass[u]) {
+          if (pos < cap) *reinterpret_cast<int2*>(slots[m] + 2 * pos) = int2{s[u], jl + u};
+          ++pos;
+        }
+      }
+      run[m] += tot;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (col == 0 && tt.tok[m] < a.n_q) a.counts[(int64_t)tt.tok[m] * a.plan.n_spans + span_idx] = run[m];
 }
 
 }  // namespace
@@ -142,6 +347,19 @@ hipError_t launch_indexer(const IndexerArgs& a_in, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL(indexer_kernel<false>, grid, dim3(256), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_threshold(const FusedArgs& a, hipStream_t stream) {
+  if (a.n_q <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_threshold_kernel, dim3((a.n_q + 3) / 4), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_collect(const FusedArgs& a, hipStream_t stream) {
+  if (a.n_q <= 0) return hipSuccess;
+  dim3 grid(a.plan.n_spans, (a.n_q + kQTile - 1) / kQTile);
+  hipLaunchKernelGGL(collect_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

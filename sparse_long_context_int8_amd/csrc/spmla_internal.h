@@ -46,6 +46,49 @@ struct TopkArgs {
   int32_t top_k;
 };
 
+// Selection for long histories without a materialized score band
+// (indexer -> top-k handoff): a sampled pass sets a per-token score
+// threshold, a collect pass recomputes exact scores and keeps the candidates
+// at or above it in fixed per-(token, span) slots, a finish pass selects and
+// sorts them exactly, and tokens whose candidates do not provably contain the
+// top-k (too few, or a slot overflowed) are redone from recomputed scores.
+struct FusedPlan {
+  int32_t span;     // compressed rows per collect workgroup (multiple of 64)
+  int32_t n_spans;  // ceil(n_comp / span)
+  int32_t cap;      // candidate slots per (token, span)
+  int32_t stride;   // sampling stride of the threshold pass
+  int32_t rank;     // sample rank whose bin sets the threshold
+};
+
+struct FusedArgs {
+  const int8_t* iq;  // [n_q][4][64]
+  const int8_t* iw;  // [n_q][4]
+  const int8_t* ik;  // [n_comp][64]
+  int32_t* sel;      // [n_q][top_k]
+  int32_t* n_sel;    // [n_q] or null
+  int32_t n_q;
+  int32_t q_pos0;
+  int32_t n_comp;
+  int32_t ratio;
+  int32_t top_k;
+  FusedPlan plan;
+  // Workspace (fused_workspace_bytes): thresh [n_q], the recompute list
+  // (n_redo, redo_list [n_q]), counts [n_q][n_spans] and
+  // cand [n_q][n_spans][cap] x (score, row).
+  int32_t* thresh;
+  int32_t* n_redo;
+  int32_t* redo_list;
+  int32_t* counts;
+  int32_t* cand;
+};
+
+// Whether the fused selection serves this launch (every token sees many
+// more rows than it keeps), its plan, and its workspace.
+bool fused_applies(int n_q, int q_pos0, int n_comp, int ratio, int top_k);
+FusedPlan fused_plan(int n_comp, int top_k);
+size_t fused_workspace_bytes(int n_q, const FusedPlan& p);
+void fused_bind_workspace(FusedArgs& a, void* ws);
+
 struct AttnArgs {
   const _Float16* q;        // [n_q][16][576]
   const _Float16* kv_comp;  // [n_comp][576]
@@ -65,6 +108,10 @@ struct AttnArgs {
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_fused_topk(const FusedArgs& a, hipStream_t stream);
+// Parts of the fused selection that compute indexer scores (indexer.hip).
+hipError_t launch_sample_threshold(const FusedArgs& a, hipStream_t stream);
+hipError_t launch_collect(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace spmla

@@ -5,8 +5,9 @@
 // the selected-row order is preserved. Order: score descending, then lower
 // row index; fewer than k visible rows are all taken and the rest is -1.
 //
-// One workgroup per query token; its visible scores stay in registers (PER
-// per thread). Every row gets a unique integer key encoding both rules,
+// One workgroup per query token; its elements (visible scores, or the
+// candidates of the fused selection) stay in registers, PER per thread.
+// Every row gets a unique integer key encoding both rules,
 //     key = ((score - min_score) << ebits) | (n_vis - 1 - row),
 // so "the k largest keys" is exactly the selection and "keys descending" is
 // exactly the output order.
@@ -15,9 +16,10 @@
 //      atomic contention low for bell-shaped score distributions);
 //   2. refinement: MSD radix select over the remaining key bits, only for
 //      the rows in that bin (usually a handful);
-//   3. the winners (padded with zeros to a power of two S >= BLOCK) are
-//      sorted by a compile-time bitonic network: pairs inside a thread in
-//      registers, across lanes with swizzles, across waves through LDS.
+//   3. ordering: the winners are bucketed by the top 11 bits of their key
+//      offset, bucket offsets come from one prefix scan, and each winner's
+//      place inside its bucket is the number of larger keys in the bucket
+//      (buckets hold a few keys for spread-out scores).
 // Integer only: exact, and independent of thread timing.
 #include "spmla_internal.h"
 
@@ -26,7 +28,7 @@ namespace {
 
 typedef unsigned long long u64;
 
-constexpr int kBins1 = 2048;  // coarse-pass bins (11 bits)
+constexpr int kBins1 = 2048;  // coarse-pass and ordering bins (11 bits)
 constexpr int kBits1 = 11;
 
 __device__ __forceinline__ int wave_max_i(int v) {
@@ -47,86 +49,6 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   }
   return v;
 }
-// 64-bit value of lane (lane ^ M) of the same wave.
-template <int M>
-__device__ __forceinline__ u64 lane_xor(u64 v) {
-  unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
-  if constexpr (M < 32) {
-    // ds_swizzle bit-mask mode: source lane = lane ^ M inside each 32 lanes
-    constexpr int kPat = (M << 10) | 0x1f;
-    lo = (unsigned)__builtin_amdgcn_ds_swizzle((int)lo, kPat);
-    hi = (unsigned)__builtin_amdgcn_ds_swizzle((int)hi, kPat);
-  } else {
-    lo = __shfl_xor(lo, 32);
-    hi = __shfl_xor(hi, 32);
-  }
-  return ((u64)hi << 32) | lo;
-}
-
-// Bitonic network sorting S = BLOCK*E keys descending, fully unrolled.
-// Thread t holds positions t*E .. t*E+E-1. A compare-exchange whose partner
-// is in the same thread runs in registers, one in another lane of the wave
-// runs through a lane swizzle, and one in another wave goes through LDS
-// (two alternating buffers of S keys, one barrier per step).
-template <int BLOCK, int E>
-struct BitonicDesc {
-  static constexpr int S = BLOCK * E;
-
-  template <int SIZE, int STRIDE>
-  __device__ static __forceinline__ void step(u64 (&v)[E], u64* buf, int tid, int& flip) {
-    if constexpr (STRIDE < E) {
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        if (i & STRIDE) continue;
-        const bool desc = ((tid * E + i) & SIZE) == 0;
-        const u64 x = v[i], y = v[i + STRIDE];
-        const bool sw = desc ? (x < y) : (x > y);
-        v[i] = sw ? y : x;
-        v[i + STRIDE] = sw ? x : y;
-      }
-    } else {
-      u64 p[E];
-      if constexpr (STRIDE < 64 * E) {
-#pragma unroll
-        for (int i = 0; i < E; ++i) p[i] = lane_xor<STRIDE / E>(v[i]);
-      } else {
-        u64* b = buf + flip * S;
-#pragma unroll
-        for (int i = 0; i < E; ++i) b[tid * E + i] = v[i];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < E; ++i) p[i] = b[(tid * E + i) ^ STRIDE];
-        flip ^= 1;
-      }
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const int e = tid * E + i;
-        const bool keep_max = ((e & SIZE) == 0) == ((e & STRIDE) == 0);
-        const u64 hi = v[i] > p[i] ? v[i] : p[i];
-        const u64 lo = v[i] > p[i] ? p[i] : v[i];
-        v[i] = keep_max ? hi : lo;
-      }
-    }
-  }
-
-  template <int SIZE, int STRIDE>
-  __device__ static __forceinline__ void merge(u64 (&v)[E], u64* buf, int tid, int& flip) {
-    step<SIZE, STRIDE>(v, buf, tid, flip);
-    if constexpr (STRIDE > 1) merge<SIZE, STRIDE / 2>(v, buf, tid, flip);
-  }
-
-  template <int SIZE>
-  __device__ static __forceinline__ void sort_from(u64 (&v)[E], u64* buf, int tid, int& flip) {
-    merge<SIZE, SIZE / 2>(v, buf, tid, flip);
-    if constexpr (SIZE < S) sort_from<SIZE * 2>(v, buf, tid, flip);
-  }
-
-  // buf: 2*S keys of LDS. Every thread of the block must call this.
-  __device__ static __forceinline__ void sort(u64 (&v)[E], u64* buf, int tid) {
-    int flip = 0;
-    if constexpr (S > 1) sort_from<2>(v, buf, tid, flip);
-  }
-};
 
 // Bins are scanned from the top. Finds the bin b in which the running count
 // of elements above first reaches `need`; returns it through shared slots.
@@ -134,7 +56,6 @@ struct BitonicDesc {
 template <int BLOCK>
 __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, int* s_bin, int* s_above,
                                          int* s_count, int* red) {
-  constexpr int NW = BLOCK / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (nbins + BLOCK - 1) / BLOCK;
   // Thread t owns bins [nbins-1 - t*per, ...) going down.
@@ -163,22 +84,30 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, i
       above += c;
     }
   }
-  (void)NW;
   __syncthreads();
 }
 
-template <int BLOCK, int PER, int E>
-__global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a) {
+// Where a workgroup's elements come from.
+enum Src : int {
+  kDense = 0,      // row r of the score matrix: element e is row e
+  kCandidate = 1,  // (score, row) candidates of the fused selection
+  kRecompute = 2,  // scores recomputed from the indexer inputs (listed tokens)
+};
+
+// Selection and ordering for token r of the launch. LDS: `keys` holds
+// 2 * top_k keys (winners, then their bucketed copy).
+template <int BLOCK, int PER, int SRC>
+__device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f, int r) {
   constexpr int NW = BLOCK / 64;
-  constexpr int S = BLOCK * E;  // sort size
   __shared__ int hist[kBins1];
+  __shared__ int boff[kBins1];
   __shared__ int red_a[NW], red_b[NW], red_c[NW];
   __shared__ int s_bin, s_above, s_count, s_cnt;
-  extern __shared__ u64 keys[];  // 2*S entries
+  __shared__ int aux[BLOCK + 1];  // span offsets (candidates) or the query row (recompute)
+  extern __shared__ u64 keys[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int r = blockIdx.x;
   const int t = a.q_pos0 + r;
   const int nv = min(a.n_comp, (t + 1) / a.ratio);
   const int k = a.top_k;
@@ -191,15 +120,104 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a) {
     return;
   }
 
-  // Scores of this token in registers; element e = i*BLOCK + tid.
-  const int32_t* row = a.scores + (int64_t)r * a.ld_scores;
+  // Elements of this token in registers; element e = i*BLOCK + tid, n_el of
+  // them. Dense and recomputed elements are rows 0 .. nv-1 in order;
+  // candidates carry their row.
   int sc[PER];
+  int jx[SRC == kCandidate ? PER : 1];
+  int n_el = nv;
+  if constexpr (SRC == kDense) {
+    const int32_t* row = a.scores + (int64_t)r * a.ld_scores;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = i * BLOCK + tid;
+      sc[i] = e < nv ? __builtin_nontemporal_load(row + e) : INT32_MIN;
+    }
+  } else if constexpr (SRC == kRecompute) {
+    // S[t][j] = sum_h w[t][h] * max(0, <iq[t][h][:], ik[j][:]>), exact.
+    const int* qrow = reinterpret_cast<const int*>(f.iq + (int64_t)r * kIdxHeads * kIdxDim);
+    if (tid < kIdxHeads * kIdxDim / 4) aux[tid] = qrow[tid];
+    if (tid == 0) aux[kIdxHeads * kIdxDim / 4] = *reinterpret_cast<const int*>(f.iw + (int64_t)r * kIdxHeads);
+    __syncthreads();
+    const int wpack = aux[kIdxHeads * kIdxDim / 4];
+#pragma unroll 1
+    for (int i = 0; i < PER; ++i) {
+      const int e = i * BLOCK + tid;
+      sc[i] = INT32_MIN;
+      if (e < nv) {
+        const int4* krow = reinterpret_cast<const int4*>(f.ik + (int64_t)e * kIdxDim);
+        int kv[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int4 v = krow[c];
+          kv[4 * c] = v.x;
+          kv[4 * c + 1] = v.y;
+          kv[4 * c + 2] = v.z;
+          kv[4 * c + 3] = v.w;
+        }
+        int tot = 0;
+#pragma unroll
+        for (int h = 0; h < kIdxHeads; ++h) {
+          int d = 0;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) d = __builtin_amdgcn_sdot4(aux[16 * h + c], kv[c], d, false);
+          tot += (int)(int8_t)((wpack >> (8 * h)) & 0xff) * max(d, 0);
+        }
+        sc[i] = tot;
+      }
+    }
+  } else {
+    // Candidates: per-span slot counts -> offsets. The token goes on the
+    // recompute list if a span overflowed its slots, if fewer than nsel
+    // candidates exist (the threshold was too high), or if they do not fit
+    // this workgroup: then they are not provably a superset of the top-k.
+    const int ns = f.plan.n_spans;  // <= BLOCK (host-checked)
+    const int cap = f.plan.cap;
+    const int cnt = tid < ns ? f.counts[(int64_t)r * ns + tid] : 0;
+    const int held = min(cnt, cap);
+    const int incl = wave_incl_scan(held, lane);
+    if (lane == 63) red_a[wave] = incl;
+    const unsigned long long over = __ballot(cnt > cap);
+    if (lane == 0) red_b[wave] = over ? 1 : 0;
+    __syncthreads();
+    int before = 0, total = 0, any_over = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      before += w < wave ? red_a[w] : 0;
+      total += red_a[w];
+      any_over |= red_b[w];
+    }
+    if (tid < ns) aux[tid] = before + incl - held;
+    const bool fail = any_over || total < nsel || total > BLOCK * PER;
+    if (fail) {
+      if (tid == 0) f.redo_list[atomicAdd(f.n_redo, 1)] = r;
+      return;
+    }
+    __syncthreads();
+    n_el = total;
+    const int32_t* cand_row = f.cand + 2 * ((int64_t)r * ns * cap);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = i * BLOCK + tid;
+      sc[i] = INT32_MIN;
+      jx[i] = 0;
+      if (e < n_el) {
+        int lo = 0, hi = ns - 1;  // last span whose offset is <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (aux[mid] <= e) lo = mid;
+          else hi = mid - 1;
+        }
+        const int2 c = *reinterpret_cast<const int2*>(cand_row + 2 * ((int64_t)lo * cap + (e - aux[lo])));
+        sc[i] = c.x;
+        jx[i] = c.y;
+      }
+    }
+  }
   int vmax = INT32_MIN, vmin = INT32_MAX;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = i * BLOCK + tid;
-    sc[i] = e < nv ? __builtin_nontemporal_load(row + e) : INT32_MIN;
-    if (e < nv) {
+    if (i * BLOCK + tid < n_el) {
       vmax = max(vmax, sc[i]);
       vmin = min(vmin, sc[i]);
     }
@@ -219,16 +237,17 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a) {
     vmin = min(vmin, red_b[w]);
   }
   const int ebits = nv > 1 ? 32 - __clz(nv - 1) : 0;
+  const u64 emask = ebits ? ((1ull << ebits) - 1) : 0ull;
   const unsigned span = (unsigned)vmax - (unsigned)vmin;  // exact: vmax >= vmin
   const int sbits = span ? 32 - __clz(span) : 0;
   auto key_of = [&](int i) -> u64 {
-    const int e = i * BLOCK + tid;
+    const int j = SRC == kCandidate ? jx[i] : i * BLOCK + tid;
     const u64 s = (unsigned)sc[i] - (unsigned)vmin;
-    return (s << ebits) | (u64)(nv - 1 - e);
+    return (s << ebits) | (u64)(nv - 1 - j);
   };
 
   u64 thresh = 0;  // selected iff key >= thresh
-  if (nv > k) {
+  if (n_el > nsel) {  // then nsel == k
     // 1. coarse pass on the top kBits1 bits of (score - min).
     const int sh1 = sbits > kBits1 ? sbits - kBits1 : 0;
     for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
@@ -236,7 +255,7 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = i * BLOCK + tid;
-      if (e < nv) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
+      if (e < n_el) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
     }
     __syncthreads();
     find_bin<BLOCK>(hist, kBins1, k, &s_bin, &s_above, &s_count, red_c);
@@ -260,7 +279,7 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
           const int e = i * BLOCK + tid;
-          if (e < nv) {
+          if (e < n_el) {
             const u64 key = key_of(i);
             if ((key >> top) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << dbits) - 1)], 1);
           }
@@ -279,86 +298,186 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a) {
     }
   }
 
-  // Collect the nsel winners into keys[0 .. nsel); stored as key + 1 so that
-  // the zero padding up to S sorts after every real entry.
-  if (tid == 0) s_cnt = 0;
-  for (int i = tid; i < S; i += BLOCK) keys[i] = 0;
+  // 3. Collect the nsel winners into keys[0 .. nsel) (one LDS atomic per
+  // wave and register, lanes take consecutive slots) and count them per
+  // ordering bucket: the top 11 bits of (key - thresh); no winner key
+  // exceeds key_hi.
+  const u64 key_hi = ((u64)span << ebits) | emask;
+  const u64 kspan = key_hi - thresh;
+  const int kbits = kspan ? 64 - __clzll(kspan) : 0;
+  const int shb = kbits > kBits1 ? kbits - kBits1 : 0;
   __syncthreads();
-  // One LDS atomic per wave and register: lanes take consecutive slots.
+  if (tid == 0) s_cnt = 0;
+  for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
+  __syncthreads();
   const u64 below = (1ull << lane) - 1;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = i * BLOCK + tid;
-    const bool take = e < nv && key_of(i) >= thresh;
+    const bool take = e < n_el && key_of(i) >= thresh;
     const u64 m = __ballot(take);
     if (m == 0) continue;  // wave-uniform
     int base = 0;
     if (lane == 0) base = atomicAdd(&s_cnt, __popcll(m));
     base = __shfl(base, 0);
     const int pos = base + __popcll(m & below);
-    if (take && pos < S) keys[pos] = key_of(i) + 1;  // pos < nsel <= S by construction
+    if (take && pos < k) {  // pos < nsel <= k by construction
+      const u64 key = key_of(i);
+      keys[pos] = key;
+      atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+    }
   }
   __syncthreads();
 
-  // 3. sort descending; thread t ends up holding ranks t*E .. t*E+E-1.
-  u64 v[E];
+  // Bucket offsets, largest bucket first: boff[b] = winners in buckets > b;
+  // hist[] becomes the fill cursor of each bucket.
+  {
+    constexpr int kPer = kBins1 / BLOCK;
+    int tot = 0;
 #pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = keys[tid * E + i];
-  BitonicDesc<BLOCK, E>::sort(v, keys, tid);
-
-  const u64 emask = ebits ? ((1ull << ebits) - 1) : 0ull;
+    for (int i = 0; i < kPer; ++i) tot += hist[kBins1 - 1 - (tid * kPer + i)];
+    const int incl = wave_incl_scan(tot, lane);
+    if (lane == 63) red_c[wave] = incl;
+    __syncthreads();
+    int base = incl - tot;
+    for (int w = 0; w < wave; ++w) base += red_c[w];
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int rank = tid * E + i;
-    if (rank < k) sel_row[rank] = rank < nsel ? (nv - 1) - (int)((v[i] - 1) & emask) : -1;
+    for (int i = 0; i < kPer; ++i) {
+      const int b = kBins1 - 1 - (tid * kPer + i);
+      const int c = hist[b];
+      boff[b] = base;
+      hist[b] = base;
+      base += c;
+    }
   }
-  for (int i = S + tid; i < k; i += BLOCK) sel_row[i] = -1;  // only when k > S
+  __syncthreads();
+  u64* bucketed = keys + k;
+  for (int e = tid; e < nsel; e += BLOCK) {
+    const u64 key = keys[e];
+    bucketed[atomicAdd(&hist[(int)((key - thresh) >> shb)], 1)] = key;
+  }
+  __syncthreads();
+  // Place of a winner = its bucket's offset + larger keys in the bucket.
+  for (int p = tid; p < nsel; p += BLOCK) {
+    const u64 key = bucketed[p];
+    const int b = (int)((key - thresh) >> shb);
+    const int st = boff[b], en = hist[b];
+    int rank = 0;
+    for (int q = st; q < en; ++q) rank += bucketed[q] > key ? 1 : 0;
+    sel_row[st + rank] = (nv - 1) - (int)(key & emask);
+  }
+  for (int i = nsel + tid; i < k; i += BLOCK) sel_row[i] = -1;
   if (a.n_sel && tid == 0) a.n_sel[r] = nsel;
 }
 
-// Sort size for a launch: at least one element per thread, and at least the
-// most winners any query of the launch can have.
-inline int sort_size(int block, int top_k, int n_comp) {
-  const int m = min(top_k, n_comp);
-  int s = block;
-  while (s < m) s <<= 1;
-  return s;
+// One workgroup per token; the recompute pass instead walks the list of
+// tokens the candidate pass could not settle.
+template <int BLOCK, int PER, int SRC>
+__global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a, FusedArgs f) {
+  if constexpr (SRC == kRecompute) {
+    const int n = *f.n_redo;
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+      topk_token<BLOCK, PER, SRC>(a, f, f.redo_list[i]);
+      __syncthreads();  // LDS is reused by the next token
+    }
+  } else {
+    topk_token<BLOCK, PER, SRC>(a, f, blockIdx.x);
+  }
 }
 
-template <int BLOCK, int PER, int E>
-hipError_t launch_e(const TopkArgs& a, hipStream_t stream) {
-  // keys[S] plus the second buffer of the cross-wave exchange.
-  const size_t lds = 2 * sizeof(u64) * (size_t)(BLOCK * E);
-  hipLaunchKernelGGL((topk_kernel<BLOCK, PER, E>), dim3(a.n_q), dim3(BLOCK), lds, stream, a);
+template <int BLOCK, int PER, int SRC>
+hipError_t launch_cfg(const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
+  // keys: the winners and their bucketed copy.
+  const size_t lds = 2 * sizeof(u64) * (size_t)a.top_k;
+  hipLaunchKernelGGL((topk_kernel<BLOCK, PER, SRC>), dim3(grid), dim3(BLOCK), lds, stream, a, f);
   return hipGetLastError();
 }
 
-template <int BLOCK, int PER>
-hipError_t launch_cfg(const TopkArgs& a, hipStream_t stream) {
-  const int e = sort_size(BLOCK, a.top_k, a.n_comp) / BLOCK;
-  switch (e) {
-    case 1: return launch_e<BLOCK, PER, 1>(a, stream);
-    case 2: return launch_e<BLOCK, PER, 2>(a, stream);
-    case 4: return launch_e<BLOCK, PER, 4>(a, stream);
-    // S <= BLOCK*PER since n_comp <= BLOCK*PER for this configuration
-    case 8: if constexpr (8 <= PER && BLOCK * 8 <= 4096) return launch_e<BLOCK, PER, 8>(a, stream); break;
-    case 16: if constexpr (16 <= PER && BLOCK * 16 <= 4096) return launch_e<BLOCK, PER, 16>(a, stream); break;
-    default: break;
-  }
-  return hipErrorInvalidValue;  // unreachable: top_k <= 4096 is host-checked
+// Block and elements per thread for `n` elements per token.
+template <int SRC>
+hipError_t launch_by_size(int n, const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
+  if (n <= 256 * 4) return launch_cfg<256, 4, SRC>(a, f, grid, stream);
+  if (n <= 256 * 8) return launch_cfg<256, 8, SRC>(a, f, grid, stream);
+  if (n <= 512 * 8) return launch_cfg<512, 8, SRC>(a, f, grid, stream);
+  if (n <= 1024 * 8) return launch_cfg<1024, 8, SRC>(a, f, grid, stream);
+  if (n <= 1024 * 16) return launch_cfg<1024, 16, SRC>(a, f, grid, stream);
+  return launch_cfg<1024, 32, SRC>(a, f, grid, stream);  // n <= 32768 (host-checked)
 }
+
+constexpr int kFinishBlock = 256;
+constexpr int kFinishPer = 16;  // candidates a finish workgroup holds: 4096
+constexpr int kRedoGrid = 128;  // workgroups that share the recompute list
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.n_q <= 0) return hipSuccess;
-  const int nc = a.n_comp;
-  if (nc <= 256 * 4) return launch_cfg<256, 4>(a, stream);
-  if (nc <= 256 * 8) return launch_cfg<256, 8>(a, stream);
-  if (nc <= 512 * 8) return launch_cfg<512, 8>(a, stream);
-  if (nc <= 1024 * 8) return launch_cfg<1024, 8>(a, stream);
-  if (nc <= 1024 * 16) return launch_cfg<1024, 16>(a, stream);
-  return launch_cfg<1024, 32>(a, stream);  // n_comp <= 32768 (host-checked)
+  return launch_by_size<kDense>(a.n_comp, a, FusedArgs{}, a.n_q, stream);
+}
+
+// The fused selection serves a launch when every token keeps at most 2048 of
+// more than 4096 visible rows and sees at least 8 rows per kept row, so that
+// the 1-in-8 sample holds enough rows above the threshold.
+bool fused_applies(int n_q, int q_pos0, int n_comp, int ratio, int top_k) {
+  if (n_q <= 0 || top_k > 2048) return false;
+  const int nv_min = min(n_comp, (q_pos0 + 1) / ratio);
+  return nv_min > 4096 && nv_min >= 8 * top_k;
+}
+
+FusedPlan fused_plan(int n_comp, int top_k) {
+  FusedPlan p;
+  p.span = 512;
+  p.n_spans = (n_comp + p.span - 1) / p.span;  // <= 64 <= finish block
+  p.cap = p.span / 4;                         // about 2.5x the expected count
+  p.stride = 8;
+  // The sample holds about k/8 rows above the k-th score; asking for four
+  // standard deviations more makes a threshold below it very likely.
+  const int base = (top_k + p.stride - 1) / p.stride;
+  int sd = 1;
+  while (sd * sd < base) ++sd;
+  p.rank = base + 4 * sd + 16;
+  return p;
+}
+
+size_t fused_workspace_bytes(int n_q, const FusedPlan& p) {
+  const size_t nq = (size_t)n_q;
+  return align256(nq * 4) + align256(4) + align256(nq * 4) + align256(nq * p.n_spans * 4) +
+         align256(nq * p.n_spans * p.cap * 8);
+}
+
+void fused_bind_workspace(FusedArgs& a, void* ws) {
+  char* w = static_cast<char*>(ws);
+  const size_t nq = (size_t)a.n_q;
+  a.thresh = reinterpret_cast<int32_t*>(w);
+  w += align256(nq * 4);
+  a.n_redo = reinterpret_cast<int32_t*>(w);
+  w += align256(4);
+  a.redo_list = reinterpret_cast<int32_t*>(w);
+  w += align256(nq * 4);
+  a.counts = reinterpret_cast<int32_t*>(w);
+  w += align256(nq * a.plan.n_spans * 4);
+  a.cand = reinterpret_cast<int32_t*>(w);
+}
+
+hipError_t launch_fused_topk(const FusedArgs& f, hipStream_t stream) {
+  if (f.n_q <= 0) return hipSuccess;
+  TopkArgs a{};
+  a.sel = f.sel;
+  a.n_sel = f.n_sel;
+  a.n_q = f.n_q;
+  a.q_pos0 = f.q_pos0;
+  a.n_comp = f.n_comp;
+  a.ratio = f.ratio;
+  a.top_k = f.top_k;
+  hipError_t e = launch_sample_threshold(f, stream);  // also clears the recompute list
+  if (e != hipSuccess) return e;
+  e = launch_collect(f, stream);
+  if (e != hipSuccess) return e;
+  e = launch_cfg<kFinishBlock, kFinishPer, kCandidate>(a, f, f.n_q, stream);
+  if (e != hipSuccess) return e;
+  return launch_by_size<kRecompute>(f.n_comp, a, f, f.n_q < kRedoGrid ? f.n_q : kRedoGrid, stream);
 }
 
 }  // namespace spmla

@@ -216,6 +216,35 @@ def test_edge_cases(sp, name, w):
     assert_close(o2.cpu().numpy(), ref["out"], f"{name} prefill out")
 
 
+@pytest.mark.parametrize("case", ["zero-queries-on-even-tokens", "sample-misleading-keys"])
+def test_fused_selection_recompute_paths(sp, case):
+    """Long history (every token sees ~30K rows, keeps 2,048): the sampled
+    threshold is wrong on purpose for some tokens, through overflowing
+    candidate slots (all scores tie at 0) or through a 1-in-8 sample that sees
+    twice the true share of high rows, so those tokens must be redone from
+    recomputed scores; indices stay bit-exact either way."""
+    w = workloads.LayerShape("fused", n_q=48, q_pos0=120000, window=16, top_k=2048)
+    say(f"[parity fused] {case}")
+    x = workloads.generate(w, seed=11)
+    if case == "zero-queries-on-even-tokens":
+        x["iq"][0::2] = 0
+    else:
+        ik = np.full_like(x["ik"], -8)
+        ik[0::16] = 7
+        x["ik"] = ik
+        x["iq"][:] = 7
+    dev = to_dev(x)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    import torch
+
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"fused {case} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"fused {case} lse")
+
+
 def test_topk_heavy_ties(sp):
     """Scores from a handful of values: the index tie-break decides most rows."""
     import torch
