@@ -261,8 +261,12 @@ def main():
         "step_ms_median": round(float(np.median(per_step)), 4),
         "step_ms_min": round(float(np.min(per_step)), 4),
         "wall_s": round(wall, 3),
-        "kernels_ms_per_band": {"indexer": round(t_idx, 4), "topk": round(t_topk, 4),
-                                "attn": round(t_attn, 4)},
+        # The three step-wise ABI calls per band (indexer_scores writes the
+        # full score band; spmla_prefill may select without it), and what a
+        # prefill step spends per band outside attention.
+        "abi_calls_ms_per_band": {"indexer_scores": round(t_idx, 4), "topk": round(t_topk, 4),
+                                  "sparse_attn": round(t_attn, 4)},
+        "prefill_selection_ms_per_band": round(ms_per_step / n_bands - t_attn, 4),
         "roofline": roofline,
         "cpu_baseline": None,
     }
