@@ -6,6 +6,7 @@ import this package. The HIP library never calls it and shares no code with it.
 from .spmla_oracle import (  # noqa: F401
     INVISIBLE,
     attend_one,
+    compress_rows,
     indexer_scores,
     key_rows,
     n_compressed,

@@ -153,6 +153,26 @@ def sparse_attention(q, kv_comp, kv_raw, sel, n_sel, q_pos0: int, window: int,
     return out, lse
 
 
+# ---------------------------------------------------- ratio-4 compression
+def compress_rows(kv_raw, ratio: int, begin: int = 0) -> np.ndarray:
+    """Compressed rows begin .. n_comp-1 built from the raw rows.
+
+    Page "perf(ds4): extend sparse prefill scheduling to 10K", Summary: the
+    indexer and attention read ratio-4 compressed rows, kept in F16, and state
+    is committed in chronological order. Reading (the pages never print the
+    formula): row j is the mean of raw rows ratio*j .. ratio*j+ratio-1, rounded
+    once to fp16 (round to nearest, ties to even); only complete groups exist,
+    so the n_raw mod ratio newest raw rows are not compressed yet.
+    The fp64 sum of four fp16 values is exact (each is a multiple of 2^-24
+    below 2^16, so the sum is an integer multiple of 2^-24 below 2^42), and
+    multiplying by 1/4 is exact, so the only rounding is the final one.
+    """
+    n_comp = n_compressed(kv_raw.shape[0], ratio)
+    groups = kv_raw[ratio * begin: ratio * n_comp].astype(np.float64)
+    groups = groups.reshape(n_comp - begin, ratio, kv_raw.shape[1])
+    return (groups.sum(axis=1) * (1.0 / ratio)).astype(np.float16)
+
+
 # -------------------------------------------------------------- whole layer
 def prefill(inputs: dict, *, q_pos0: int, ratio: int, window: int, top_k: int,
             scale: float, d_v: int, q_begin: int = 0, q_end: int | None = None,

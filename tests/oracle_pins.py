@@ -382,6 +382,94 @@ def pin_band_independence(orc):
         np.testing.assert_array_equal(full[key], np.concatenate([p[key] for p in parts]))
 
 
+# ------------------------------------------------------ compression pins
+def _fp16_bits_exact(v):
+    """IEEE binary16 bits of the exact rational v rounded to nearest, ties
+    to even (from the format's definition; v is finite and |v| <= 65504)."""
+    from fractions import Fraction
+
+    def rne(x):
+        fl = x.numerator // x.denominator
+        d = x - fl
+        if d > Fraction(1, 2):
+            return fl + 1
+        if d < Fraction(1, 2):
+            return fl
+        return fl + (fl & 1)
+
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = 0
+    while a >= Fraction(2) ** (e + 1):
+        e += 1
+    while a < Fraction(2) ** e:
+        e -= 1
+    if e < -14:  # subnormal: multiples of 2^-24
+        m = rne(a * 2 ** 24)
+        return sign | m  # m == 1024 is the smallest normal's encoding
+    m = rne(a * Fraction(2) ** (10 - e))
+    if m == 2048:
+        m, e = 1024, e + 1
+    return sign | ((e + 15) << 10) | (m - 1024)
+
+
+def _fp16_value(bits):
+    from fractions import Fraction
+
+    s = -1 if bits & 0x8000 else 1
+    e = (bits >> 10) & 31
+    m = bits & 1023
+    if e == 0:
+        return s * Fraction(m, 2 ** 24)
+    return s * Fraction(1024 + m, 2 ** 10) * Fraction(2) ** (e - 15)
+
+
+def pin_compress_exact_rounding(orc):
+    """Brute force: exact rational mean of each group, rounded by the format's
+    definition, on values that hit subnormals, ties and wide exponent spans."""
+    rng = np.random.default_rng(21)
+    n_raw, D = 4 * 9 + 3, 24  # 9 complete groups and a 3-row tail
+    bits = rng.integers(0, 0x7C00, (n_raw, D)).astype(np.uint16)  # finite
+    bits[rng.random((n_raw, D)) < 0.5] |= 0x8000
+    bits[:4, :4] = [[0x3C00, 0x1000, 0x0001, 0x0000]] * 4  # spans 2^0 .. 2^-24
+    bits[4:8, 0] = [0x0001, 0x0001, 0x0000, 0x0000]  # 2^-25: tie at zero -> +0
+    bits[4:8, 1] = [0x0001, 0x0001, 0x0001, 0x0000]  # 3 * 2^-26 -> 2^-24
+    bits[4:8, 2] = [0x7BFF, 0x7BFF, 0x7BFF, 0x7BFF]  # largest finite
+    x = bits.view(np.float16)
+    got = orc.compress_rows(x, 4).view(np.uint16)
+    assert got.shape == (9, D)
+    for j in range(9):
+        for d in range(D):
+            mean = sum(_fp16_value(int(bits[4 * j + i, d])) for i in range(4)) / 4
+            want = _fp16_bits_exact(mean)
+            if mean == 0:  # IEEE sum: -0 only when every term is -0
+                want = 0x8000 if all(int(bits[4 * j + i, d]) == 0x8000 for i in range(4)) else 0
+            assert int(got[j, d]) == want, (j, d, hex(int(got[j, d])), hex(want))
+
+
+def pin_compress_closed_forms(orc):
+    """Constant groups keep their value; a mean that lies just above a tie
+    rounds up (one rounding, no stop at float32); the tail is not compressed;
+    `begin` skips rows already committed."""
+    x = np.zeros((4 * 3 + 2, 8), np.float16)
+    x[0:4] = np.float16(1.5)
+    x[4:8] = np.float16(-3.0e-5)
+    # 1 + 2^-11 + 2^-24 over 4 = 0.25 + 2^-13 + 2^-26: just above the tie
+    # between 0.25 and 0.25 + 2^-12; float32 would round it onto the tie first.
+    x[8, 0], x[9, 0], x[10, 0] = np.float16(1.0), np.float16(2.0 ** -11), np.float16(2.0 ** -24)
+    x[12:14] = np.float16(7.0)  # tail rows (ignored)
+    c = orc.compress_rows(x, 4)
+    assert c.shape == (3, 8)
+    assert (c[0] == np.float16(1.5)).all()
+    assert (c[1] == np.float16(-3.0e-5)).all()
+    assert c[2, 0] == np.float16(0.25 + 2.0 ** -12)
+    assert (c[2, 1:] == 0).all()
+    assert (orc.compress_rows(x, 4, begin=2) == c[2:]).all()
+    assert orc.compress_rows(x[:3], 4).shape == (0, 8)
+
+
 PINS = [
     pin_visibility_brute_force,
     pin_window_brute_force,
@@ -395,4 +483,6 @@ PINS = [
     pin_attention_closed_forms,
     pin_sparse_equals_dense_sdpa,
     pin_band_independence,
+    pin_compress_exact_rounding,
+    pin_compress_closed_forms,
 ]
