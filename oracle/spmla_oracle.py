@@ -166,11 +166,17 @@ def compress_rows(kv_raw, ratio: int, begin: int = 0) -> np.ndarray:
     The fp64 sum of four fp16 values is exact (each is a multiple of 2^-24
     below 2^16, so the sum is an integer multiple of 2^-24 below 2^42), and
     multiplying by 1/4 is exact, so the only rounding is the final one.
+    Members are added one after another with IEEE fp64 addition, so a group
+    of four -0 gives -0 and exact cancellation gives +0 (numpy's sum
+    reduction would start from +0 and lose the sign of an all -0 group).
     """
     n_comp = n_compressed(kv_raw.shape[0], ratio)
     groups = kv_raw[ratio * begin: ratio * n_comp].astype(np.float64)
     groups = groups.reshape(n_comp - begin, ratio, kv_raw.shape[1])
-    return (groups.sum(axis=1) * (1.0 / ratio)).astype(np.float16)
+    total = groups[:, 0]
+    for i in range(1, ratio):
+        total = total + groups[:, i]
+    return (total * (1.0 / ratio)).astype(np.float16)
 
 
 # -------------------------------------------------------------- whole layer

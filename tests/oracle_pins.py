@@ -437,6 +437,8 @@ def pin_compress_exact_rounding(orc):
     bits[4:8, 0] = [0x0001, 0x0001, 0x0000, 0x0000]  # 2^-25: tie at zero -> +0
     bits[4:8, 1] = [0x0001, 0x0001, 0x0001, 0x0000]  # 3 * 2^-26 -> 2^-24
     bits[4:8, 2] = [0x7BFF, 0x7BFF, 0x7BFF, 0x7BFF]  # largest finite
+    bits[4:8, 3] = [0x8000, 0x8000, 0x8000, 0x8000]  # all -0 -> -0
+    bits[4:8, 4] = [0x3C00, 0xBC00, 0x8000, 0x8000]  # exact cancellation -> +0
     x = bits.view(np.float16)
     got = orc.compress_rows(x, 4).view(np.uint16)
     assert got.shape == (9, D)

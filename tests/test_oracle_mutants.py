@@ -48,13 +48,15 @@ MUTANTS = [
     ("attn-drops-a-selected-row", "sel_row[:n_sel]", "sel_row[:max(0, n_sel - 1)]"),
     ("attn-head-swap", "out[i], lse[i] = attend_one(q[r], keys, scale, d_v)",
      "out[i], lse[i] = attend_one(q[r][::-1], keys, scale, d_v)"),
-    ("compress-via-float32", "return (groups.sum(axis=1) * (1.0 / ratio)).astype(np.float16)",
-     "return (groups.sum(axis=1) * (1.0 / ratio)).astype(np.float32).astype(np.float16)"),
-    ("compress-sum-not-mean", "return (groups.sum(axis=1) * (1.0 / ratio)).astype(np.float16)",
-     "return groups.sum(axis=1).astype(np.float16)"),
+    ("compress-via-float32", "return (total * (1.0 / ratio)).astype(np.float16)",
+     "return (total * (1.0 / ratio)).astype(np.float32).astype(np.float16)"),
+    ("compress-sum-not-mean", "return (total * (1.0 / ratio)).astype(np.float16)",
+     "return total.astype(np.float16)"),
     ("compress-groups-shifted", "groups = kv_raw[ratio * begin: ratio * n_comp]",
      "groups = kv_raw[ratio * begin + 1: ratio * n_comp + 1]"),
-    ("compress-drops-a-member", "groups.sum(axis=1) * (1.0 / ratio)", "groups[:, 1:].sum(axis=1) * (1.0 / ratio)"),
+    ("compress-drops-a-member", "for i in range(1, ratio):", "for i in range(2, ratio):"),
+    ("compress-sum-reduction-sign", "    total = groups[:, 0]\n    for i in range(1, ratio):\n        total = total + groups[:, i]",
+     "    total = groups.sum(axis=1)"),
     ("prefill-query-offset", "indexer_scores(iq[a:b], iw[a:b], ik, q_pos0 + a, ratio)",
      "indexer_scores(iq[a:b], iw[a:b], ik, q_pos0, ratio)"),
 ]
