@@ -111,6 +111,40 @@ def cpu_baseline(w, x):
     }
 
 
+def bench_compress(args, sp, workloads, torch):
+    """Ratio-4 compression of every complete group of the workload's raw rows
+    (the step before the path). Algorithmic bytes per compressed row: four
+    raw rows read and one compressed row written, 5 x 1,152 B."""
+    w = workloads.BY_NAME[args.workload]
+    log(f"compress {w.name}: generating raw rows")
+    x = workloads.generate(w)
+    raw = torch.from_numpy(x["kv_raw"]).cuda()
+    d = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
+    comp = torch.empty((d.n_comp, w.d_qk), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sp.spmla_compress(d, raw, comp, 0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        sp.spmla_compress(d, raw, comp, 0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = d.n_comp * 5 * w.d_qk * 2
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "ratio-4 compression of the raw history (GB/s)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "n_raw": w.n_raw, "n_comp": d.n_comp},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "compress_kernel",
+                     "bytes_per_launch": nbytes, "launch_ms": round(ms, 4)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +154,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--op", choices=["prefill", "compress"], default="prefill",
+                    help="compress: time spmla_compress over the workload's whole raw history")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the prefill bands of one layer fit a single "
@@ -148,6 +184,9 @@ def main():
         print(json.dumps({"copy_mib": args.copy_mib, "dispatches": 3}), flush=True)
         return
     sp.load_library()
+    if args.op == "compress":
+        bench_compress(args, sp, workloads, torch)
+        return
     w = workloads.BY_NAME[args.workload]
     log(f"workload {w.name}: generating inputs")
     x = workloads.generate(w)

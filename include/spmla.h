@@ -176,6 +176,28 @@ int spmla_sparse_attn(const spmla_desc* desc, const uint16_t* q, const uint16_t*
                       void* stream);
 
 /*
+ * Ratio-4 compression of raw latent rows: the step before the path (page
+ * "perf(ds4): extend sparse prefill scheduling to 10K", Summary: ratio-4
+ * compressed rows kept in F16, state committed in chronological order).
+ *
+ *   kv_comp[j][d] = fp16( (kv_raw[4j][d] + kv_raw[4j+1][d] + kv_raw[4j+2][d]
+ *                          + kv_raw[4j+3][d]) / 4 )
+ * for comp_begin <= j < n_comp, with n_comp = floor(n_raw / 4): only complete
+ * groups, so the n_raw mod 4 newest raw rows stay uncompressed until their
+ * group completes. The sum is exact and rounded once (nearest, ties to
+ * even); -0 results only from four -0 inputs; inf / NaN as in IEEE addition.
+ * Rows before comp_begin (already committed) are not touched, so a prefill
+ * that appends raw rows compresses only the groups it completed.
+ *
+ *   kv_raw   fp16  [n_raw][d_qk]   (reads rows 4*comp_begin .. 4*n_comp-1)
+ *   kv_comp  fp16  [n_comp][d_qk]  (writes rows comp_begin .. n_comp-1)
+ *   comp_begin  0 <= comp_begin <= n_comp
+ * Only desc->n_raw, n_comp, ratio (must be 4) and d_qk are used.
+ */
+int spmla_compress(const spmla_desc* desc, const uint16_t* kv_raw, uint16_t* kv_comp, int32_t comp_begin,
+                   void* stream);
+
+/*
  * Workspace bytes spmla_prefill needs for this descriptor: one band of
  * indexer scores plus one band of selected rows. Returns SPMLA_OK and
  * writes *bytes, or an error code.

@@ -25,6 +25,7 @@ __all__ = [
     "spmla_indexer_scores",
     "spmla_topk",
     "spmla_sparse_attn",
+    "spmla_compress",
     "spmla_prefill_workspace_bytes",
     "spmla_prefill",
     "prefill",
@@ -48,6 +49,7 @@ EXPORTED_SYMBOLS = [
     "spmla_indexer_scores",
     "spmla_topk",
     "spmla_sparse_attn",
+    "spmla_compress",
     "spmla_prefill_workspace_bytes",
     "spmla_prefill",
 ]
@@ -112,6 +114,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spmla_indexer_scores": (ctypes.c_int, [D, P, P, P, P, P]),
         "spmla_topk": (ctypes.c_int, [D, P, P, P, P]),
         "spmla_sparse_attn": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
+        "spmla_compress": (ctypes.c_int, [D, P, P, ctypes.c_int32, P]),
         "spmla_prefill_workspace_bytes": (ctypes.c_int, [D, ctypes.POINTER(ctypes.c_size_t)]),
         "spmla_prefill": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     }
@@ -193,6 +196,13 @@ def spmla_sparse_attn(desc, q, kv_comp, kv_raw, sel, out, lse=None, stream=None)
         ctypes.byref(desc), _ptr(q, torch.float16, "q"), _ptr(kv_comp, torch.float16, "kv_comp"),
         _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(sel, torch.int32, "sel"),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def spmla_compress(desc, kv_raw, kv_comp, comp_begin=0, stream=None) -> None:
+    torch = _dt()
+    _check(load_library().spmla_compress(
+        ctypes.byref(desc), _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(kv_comp, torch.float16, "kv_comp"),
+        ctypes.c_int32(comp_begin), _stream(stream)))
 
 
 def spmla_prefill_workspace_bytes(desc) -> int:

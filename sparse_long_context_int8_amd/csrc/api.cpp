@@ -202,6 +202,20 @@ int spmla_sparse_attn(const spmla_desc* d, const uint16_t* q, const uint16_t* kv
   return hip_status(spmla::launch_attn(a, (hipStream_t)stream), "attention launch");
 }
 
+int spmla_compress(const spmla_desc* d, const uint16_t* kv_raw, uint16_t* kv_comp, int32_t comp_begin,
+                   void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->ratio != 4) return fail(SPMLA_EUNSUPPORTED, "compression is built for ratio 4 (got %d)", d->ratio);
+  if (comp_begin < 0 || comp_begin > d->n_comp)
+    return fail(SPMLA_EINVAL, "comp_begin %d outside [0, n_comp=%d]", comp_begin, d->n_comp);
+  if (comp_begin == d->n_comp) return ok();
+  REQUIRE_PTR(kv_raw);
+  REQUIRE_PTR(kv_comp);
+  return hip_status(spmla::launch_compress(kv_raw, kv_comp, comp_begin, d->n_comp, (hipStream_t)stream),
+                    "compress launch");
+}
+
 int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
   int rc = check_desc(d);
   if (rc) return rc;

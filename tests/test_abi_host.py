@@ -141,6 +141,20 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert lib.spmla_check_desc(None) == sp.SPMLA_EINVAL
 
 
+def test_compress_arguments_checked_before_launch():
+    lib = sp.load_library()
+    d = sp.make_desc(8, 100, 16, 4)  # n_raw 108 -> n_comp 27
+    raw, comp = ctypes.c_void_p(A), ctypes.c_void_p(A)
+    assert lib.spmla_compress(ctypes.byref(d), raw, comp, -1, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_compress(ctypes.byref(d), raw, comp, 28, None) == sp.SPMLA_EINVAL
+    assert "comp_begin" in lib.spmla_last_error().decode()
+    assert lib.spmla_compress(ctypes.byref(d), None, comp, 0, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_compress(ctypes.byref(d), raw, ctypes.c_void_p(A + 2), 0, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_compress(ctypes.byref(d), raw, comp, 27, None) == 0  # nothing new: no launch
+    d8 = sp.make_desc(8, 100, 16, 4, ratio=8)
+    assert lib.spmla_compress(ctypes.byref(d8), raw, comp, 0, None) == sp.SPMLA_EUNSUPPORTED
+
+
 def test_empty_call_is_a_noop():
     lib = sp.load_library()
     d = sp.make_desc(0, 10, 64, 32)
