@@ -90,13 +90,18 @@ size_t sel_bytes_per_band(const spmla_desc* d) {
   return (size_t)rows * (size_t)d->top_k * sizeof(int32_t);
 }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-// Per-band scratch: the score band of the dense selection or the fused
-// selection's thresholds, slot counts and candidates, whichever is larger.
+// Per-band scratch, reused by the steps of a band in stream order: the score
+// band of the dense selection or the fused selection's thresholds, slot
+// counts and candidates, then the attention's key-split partials (small
+// bands only), whichever is largest.
 size_t band_scratch_bytes(const spmla_desc* d) {
   const int rows = d->band < d->n_q ? d->band : d->n_q;
-  const size_t dense = round_up(scores_bytes_per_band(d), 256);
+  size_t need = round_up(scores_bytes_per_band(d), 256);
   const size_t fused = spmla::fused_workspace_bytes(rows, spmla::fused_plan(d->n_comp, d->top_k));
-  return dense > fused ? dense : fused;
+  const size_t part = round_up(spmla::attn_partial_bytes(rows, spmla::attn_splits(d->n_q)), 256);
+  if (fused > need) need = fused;
+  if (part > need) need = part;
+  return need;
 }
 
 spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
@@ -116,6 +121,9 @@ spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t
   a.window = d->window;
   a.top_k = d->top_k;
   a.scale_log2e = (float)((double)d->scale * 1.4426950408889634);
+  a.splits = 1;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
   return a;
 }
 
@@ -311,6 +319,12 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
                                    lse ? lse + b0 * spmla::kHeads : nullptr);
     aa.n_q = bn;
     aa.q_pos0 = pos0;
+    aa.splits = spmla::attn_splits(d->n_q);
+    if (aa.splits > 1) {  // a small call: split each key list, partials in the band scratch
+      const size_t items = (size_t)bn * aa.splits;
+      aa.part_o = reinterpret_cast<float*>(ws);
+      aa.part_ml = aa.part_o + items * spmla::kHeads * spmla::kDv;
+    }
     rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
     if (rc) return rc;
   }

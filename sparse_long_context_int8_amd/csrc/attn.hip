@@ -155,11 +155,15 @@ void attn_kernel(AttnArgs a) {
   lds_char* buf1 = (lds_char*)buf1_;
   const unsigned sbuf_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)sbuf;
 
-  // Queries are dealt to the dies in contiguous blocks so that the window
-  // rows shared by neighbouring queries stay in one die's L2.
-  const int per_xcd = (a.n_q + kXcds - 1) / kXcds;
-  const int r = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (r >= a.n_q) return;
+  // Work items (query r, key split s) are dealt to the dies in contiguous
+  // blocks so that the window rows shared by neighbouring queries stay in
+  // one die's L2.
+  const int n_items = a.n_q * a.splits;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= n_items) return;
+  const int r = item / a.splits;
+  const int split = item - r * a.splits;
 
   const int t = a.q_pos0 + r;
   const int lane = threadIdx.x & 63;
@@ -172,6 +176,10 @@ void attn_kernel(AttnArgs a) {
   const int ws = max(0, t - a.window + 1);
   const int nk = nsel + (t - ws + 1);
   const int nchunks = (nk + CHUNK - 1) / CHUNK;
+  // This work item's chunks [c_begin, c_end) of the query's key list.
+  const int per_split = (nchunks + a.splits - 1) / a.splits;
+  const int c_begin = split * per_split;
+  const int c_end = min(nchunks, c_begin + per_split);
   const int32_t* sel_row = a.sel + (int64_t)r * a.top_k;
   const char* comp_base = reinterpret_cast<const char*>(a.kv_comp);
   const char* raw_base = reinterpret_cast<const char*>(a.kv_raw);
@@ -409,13 +417,25 @@ void attn_kernel(AttnArgs a) {
     if constexpr (NBUF == 1) lds_barrier();  // `cur` and sbuf are refilled next
   };
 
-  // Prologue: start the gather of chunk 0, then load Q^T while it flies.
+  if (c_begin >= c_end) {  // an empty split: a neutral partial
+    float* prow = a.part_o + ((int64_t)item * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < C::kNt; ++nt) *reinterpret_cast<float4v*>(prow + 16 * nt) = float4v{0.f, 0.f, 0.f, 0.f};
+    if (wave == 0 && g == 0) {
+      a.part_ml[((int64_t)item * kHeads + c16) * 2] = -__builtin_inff();
+      a.part_ml[((int64_t)item * kHeads + c16) * 2 + 1] = 0.f;
+    }
+    return;
+  }
+
+  // Prologue: start the gather of the first chunk, then load Q^T while it
+  // flies.
   unsigned long long valid_cur;
   half8 rope_cur[2], rope_nxt[2];
   {
-    const int sel0 = load_sel(0);
+    const int sel0 = load_sel(c_begin);
     bool ok0;
-    const char* kp0 = row_of(0, sel0, ok0);
+    const char* kp0 = row_of(c_begin, sel0, ok0);
     valid_cur = __ballot(ok0);
     gather(kp0, buf0, rope_cur);
   }
@@ -426,7 +446,7 @@ void attn_kernel(AttnArgs a) {
     for (int s = 0; s < C::kSteps; ++s)
       if (s < q_len) qf[s] = *reinterpret_cast<const half8*>(qrow + 32 * (q_start + s));
   }
-  int sel_next = load_sel(min(1, nchunks - 1));
+  int sel_next = load_sel(min(c_begin + 1, c_end - 1));
 
   if constexpr (NBUF == 2) {
     // Chunk ch computes from `cur` while the gather of chunk ch+1 lands in
@@ -436,11 +456,11 @@ void attn_kernel(AttnArgs a) {
       wait_vmcnt<0>();
       lds_barrier();
       unsigned long long valid_next = 0;
-      if (ch + 1 < nchunks) {
+      if (ch + 1 < c_end) {
         bool okn;
         const char* kpn = row_of(ch + 1, sel_next, okn);
         valid_next = __ballot(okn);
-        sel_next = load_sel(min(ch + 2, nchunks - 1));
+        sel_next = load_sel(min(ch + 2, c_end - 1));
         gather(kpn, nxt, rope_nxt);
       }
       compute(cur, valid_cur, rope_cur, ch & 1);
@@ -448,22 +468,22 @@ void attn_kernel(AttnArgs a) {
       rope_cur[0] = rope_nxt[0];
       rope_cur[1] = rope_nxt[1];
     };
-    for (int ch = 0;;) {
+    for (int ch = c_begin;;) {
       step(ch, buf0, buf1);
-      if (++ch >= nchunks) break;
+      if (++ch >= c_end) break;
       step(ch, buf1, buf0);
-      if (++ch >= nchunks) break;
+      if (++ch >= c_end) break;
     }
   } else {
-    for (int ch = 0; ch < nchunks; ++ch) {
+    for (int ch = c_begin; ch < c_end; ++ch) {
       wait_vmcnt<0>();
       lds_barrier();
       compute(buf0, valid_cur, rope_cur, 0);
-      if (ch + 1 < nchunks) {
+      if (ch + 1 < c_end) {
         bool okn;
         const char* kpn = row_of(ch + 1, sel_next, okn);
         valid_cur = __ballot(okn);
-        sel_next = load_sel(min(ch + 2, nchunks - 1));
+        sel_next = load_sel(min(ch + 2, c_end - 1));
         gather(kpn, buf0, rope_cur);
       }
     }
@@ -471,6 +491,18 @@ void attn_kernel(AttnArgs a) {
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot = l_tot + __shfl_xor(l_tot, 32);
+  if (a.splits > 1) {
+    // Partial result of this split: O and l relative to the reference m
+    // (log2 units); attn_merge_kernel combines the splits of a query.
+    float* prow = a.part_o + ((int64_t)item * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < C::kNt; ++nt) *reinterpret_cast<float4v*>(prow + 16 * nt) = acc_o[nt];
+    if (wave == 0 && g == 0) {
+      a.part_ml[((int64_t)item * kHeads + c16) * 2] = m_ref;
+      a.part_ml[((int64_t)item * kHeads + c16) * 2 + 1] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   float* orow = a.out + ((int64_t)r * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
 #pragma unroll
@@ -499,15 +531,83 @@ void attn_kernel(AttnArgs a) {
 #define SPMLA_ATTN_ROPE_REG 0
 #endif
 
+// Combines the key splits of one (query, head): with M the largest split
+// reference, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and
+// lse = (M + log2 of that sum) * ln 2, splits summed in order. The split
+// weights are formed once in LDS; the partial rows are read with independent
+// loads (8 splits in flight per thread).
+constexpr int kMaxSplits = 64;
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float s_lsum, s_mmax;
+  const int r = blockIdx.x / kHeads;
+  const int h = blockIdx.x % kHeads;
+  const int tid = threadIdx.x;
+  const int ns = a.splits;  // <= kMaxSplits
+  if (tid < 64) {
+    const bool has = tid < ns;
+    const float* ml = a.part_ml + (((int64_t)r * ns + (has ? tid : 0)) * kHeads + h) * 2;
+    const float m = has ? ml[0] : -__builtin_inff();
+    const float l = has ? ml[1] : 0.f;
+    float m_max = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m_max = fmaxf(m_max, __shfl_xor(m_max, o));
+    const float w = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - m_max);
+    if (has) w_s[tid] = w;
+    // l sum in split order (a fixed order for every launch)
+    float wl = w * l;
+    float total = 0.f;
+    for (int s = 0; s < ns; ++s) total += __shfl(wl, s);
+    if (tid == 0) {
+      s_lsum = total;
+      s_mmax = m_max;
+    }
+  }
+  __syncthreads();
+  const int d = 4 * tid;
+  const float* po = a.part_o + ((int64_t)r * ns * kHeads + h) * kDv + d;
+  const int64_t stride = (int64_t)kHeads * kDv;
+  float4v o = float4v{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float4v p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const float4v*>(po + (s + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o += w_s[s + u] * p[u];
+  }
+  for (; s < ns; ++s) o += w_s[s] * *reinterpret_cast<const float4v*>(po + s * stride);
+  const float l_sum = s_lsum;
+  *reinterpret_cast<float4v*>(a.out + ((int64_t)r * kHeads + h) * kDv + d) = o * (1.0f / l_sum);
+  if (a.lse && tid == 0) a.lse[(int64_t)r * kHeads + h] = (s_mmax + __builtin_amdgcn_logf(l_sum)) * 0.69314718055994531f;
+}
+
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  if (a.n_q <= 0) return hipSuccess;
-  const int per_xcd = (a.n_q + kXcds - 1) / kXcds;
+int attn_splits(int n_q_call) {
+  if (n_q_call >= 512) return 1;
+  const int s = (1024 + n_q_call - 1) / n_q_call;
+  return s < kMaxSplits ? s : kMaxSplits;
+}
+
+size_t attn_partial_bytes(int rows, int splits) {
+  if (splits <= 1) return 0;
+  const size_t items = (size_t)rows * splits;
+  return items * kHeads * kDv * sizeof(float) + items * kHeads * 2 * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
+  if (a_in.n_q <= 0) return hipSuccess;
+  AttnArgs a = a_in;
+  if (a.splits < 1) a.splits = 1;
+  const int per_xcd = (a.n_q * a.splits + kXcds - 1) / kXcds;
   constexpr int W = SPMLA_ATTN_WAVES;
   hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE,
                                   (bool)SPMLA_ATTN_ROPE_REG>),
                      dim3(per_xcd * kXcds), dim3(64 * W), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_q * kHeads), dim3(kDv / 4), 0, stream, a);
   return hipGetLastError();
 }
 

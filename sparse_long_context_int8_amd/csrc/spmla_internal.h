@@ -104,7 +104,20 @@ struct AttnArgs {
   int32_t window;
   int32_t top_k;
   float scale_log2e;        // softmax scale * log2(e)
+  // Key splits per query (1: each workgroup does a whole query). With more,
+  // each (query, split) writes a partial O [16][512] and (m, l) [16] to
+  // part_o / part_ml, and a merge pass writes out and lse.
+  int32_t splits;
+  float* part_o;            // [n_q * splits][16][512]
+  float* part_ml;           // [n_q * splits][16][2]
 };
+
+// Key splits per query for a call of n_q_call queries (enough work items to
+// fill the chip when the call is small; a function of the whole call, so
+// results do not depend on how it is cut into bands) and the partial-result
+// bytes of `rows` queries.
+int attn_splits(int n_q_call);
+size_t attn_partial_bytes(int rows, int splits);
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);

@@ -417,11 +417,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   return launch_by_size<kDense>(a.n_comp, a, FusedArgs{}, a.n_q, stream);
 }
 
-// The fused selection serves a launch when every token keeps at most 2048 of
-// more than 4096 visible rows and sees at least 8 rows per kept row, so that
-// the 1-in-8 sample holds enough rows above the threshold.
+// The fused selection serves a launch of at least 256 tokens (fewer leave
+// its passes latency-bound, and their score band is small) when every token
+// keeps at most 2048 of more than 4096 visible rows and sees at least 8 rows
+// per kept row, so that the 1-in-8 sample holds enough rows above the
+// threshold.
 bool fused_applies(int n_q, int q_pos0, int n_comp, int ratio, int top_k) {
-  if (n_q <= 0 || top_k > 2048) return false;
+  if (n_q < 256 || top_k > 2048) return false;
   const int nv_min = min(n_comp, (q_pos0 + 1) / ratio);
   return nv_min > 4096 && nv_min >= 8 * top_k;
 }

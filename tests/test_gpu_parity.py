@@ -151,6 +151,52 @@ def test_full_size_prefill_sampled(sp, name):
     assert_close(np.array(got_lse), np.array(want_lse), f"{name} lse[sampled]")
 
 
+@pytest.mark.parametrize("name", ["decode-1-at-122878", "verify-5-at-122874"])
+def test_decode_and_verify_lanes(sp, name):
+    """1 and 5 query lanes after 122,874+ tokens: every lane against the
+    oracle; the attention of so few queries runs as key splits + merge."""
+    import torch
+
+    w = workloads.BY_NAME[name]
+    say(f"[parity decode] {name}")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"{name} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"{name} lse")
+
+
+def test_key_splits_match_whole_queries(sp):
+    """300 queries as their own call (key splits + merge) and the same
+    queries inside a 2,048-query call (one workgroup per query): equal within
+    fp32 rounding, and both within tolerance of the oracle."""
+    import torch
+
+    w = workloads.LayerShape("splits", n_q=2048, q_pos0=6000, window=128, top_k=512)
+    say("[parity] key splits vs whole queries")
+    x = workloads.generate(w, seed=13)
+    dev = to_dev(x)
+    o_full, l_full, s_full = sp.prefill(desc_of(sp, w), dev)
+    a0, n = 700, 300
+    d = sp.make_desc(n, w.q_pos0 + a0, w.window, w.top_k)
+    sub = {"q": dev["q"][a0:a0 + n], "iq": dev["iq"][a0:a0 + n], "iw": dev["iw"][a0:a0 + n],
+           "kv_raw": dev["kv_raw"][:d.n_raw], "kv_comp": dev["kv_comp"][:d.n_comp], "ik": dev["ik"][:d.n_comp]}
+    o_sub, l_sub, s_sub = sp.prefill(d, sub)
+    torch.cuda.synchronize()
+    assert torch.equal(s_full[a0:a0 + n], s_sub)
+    assert_close(o_sub.cpu().numpy(), o_full[a0:a0 + n].cpu().numpy().astype(np.float64), "splits out")
+    assert_close(l_sub.cpu().numpy(), l_full[a0:a0 + n].cpu().numpy().astype(np.float64), "splits lse")
+    rows = [0, 1, 150, 299]
+    ref = [oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k, scale=w.scale,
+                          d_v=w.d_v, q_begin=a0 + r, q_end=a0 + r + 1) for r in rows]
+    assert_close(o_sub.cpu().numpy()[rows], np.concatenate([r_["out"] for r_ in ref]), "splits out vs oracle")
+    assert_close(l_sub.cpu().numpy()[rows], np.concatenate([r_["lse"] for r_ in ref]), "splits lse vs oracle")
+
+
 # ------------------------------------------------------------- properties
 def test_deterministic_and_band_invariant(sp):
     import torch
@@ -218,12 +264,12 @@ def test_edge_cases(sp, name, w):
 
 @pytest.mark.parametrize("case", ["zero-queries-on-even-tokens", "sample-misleading-keys"])
 def test_fused_selection_recompute_paths(sp, case):
-    """Long history (every token sees ~30K rows, keeps 2,048): the sampled
+    """Long history (256 tokens, each sees ~30K rows and keeps 2,048): the sampled
     threshold is wrong on purpose for some tokens, through overflowing
     candidate slots (all scores tie at 0) or through a 1-in-8 sample that sees
     twice the true share of high rows, so those tokens must be redone from
     recomputed scores; indices stay bit-exact either way."""
-    w = workloads.LayerShape("fused", n_q=48, q_pos0=120000, window=16, top_k=2048)
+    w = workloads.LayerShape("fused", n_q=256, q_pos0=120000, window=16, top_k=2048)
     say(f"[parity fused] {case}")
     x = workloads.generate(w, seed=11)
     if case == "zero-queries-on-even-tokens":

@@ -76,7 +76,13 @@ CHUNK_8192_AT_114687 = LayerShape(
     "chunk-8192-after-114687", n_q=8192, q_pos0=114687, window=128, top_k=2048
 )
 
-WORKLOADS = [TINY_256, BAND_2048, PREFILL_8192, PREFILL_9133, CHUNK_8192_AT_114687]
+# Decode and speculative verification at the end of the same long history:
+# 1 or 5 new query tokens (lanes) whose last position is 122,878, so the
+# history is 122,879 raw rows and 30,719 compressed rows as above.
+DECODE_1 = LayerShape("decode-1-at-122878", n_q=1, q_pos0=122878, window=128, top_k=2048)
+VERIFY_5 = LayerShape("verify-5-at-122874", n_q=5, q_pos0=122874, window=128, top_k=2048)
+
+WORKLOADS = [TINY_256, BAND_2048, PREFILL_8192, PREFILL_9133, CHUNK_8192_AT_114687, DECODE_1, VERIFY_5]
 BY_NAME = {w.name: w for w in WORKLOADS}
 # Seed of each named workload: its position in WORKLOADS.
 SEEDS = {w.name: i for i, w in enumerate(WORKLOADS)}
