@@ -145,6 +145,49 @@ def bench_compress(args, sp, workloads, torch):
     }), flush=True)
 
 
+def bench_attn_grouped(args, sp, workloads, torch):
+    """Streaming (spmla_sparse_attn) against query-tiled (grouped) attention,
+    band by band on the selections spmla_prefill made, as the pages compare
+    their grouped and streaming kernels."""
+    w = workloads.BY_NAME[args.workload]
+    log(f"attn-grouped {w.name}: generating inputs")
+    x = workloads.generate(w)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in x.items()}
+    desc = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
+    out, lse, sel = sp.prefill(desc, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n_bands = sp.spmla_num_bands(desc)
+    res = {}
+    for name, fn in (("streaming", sp.spmla_sparse_attn), ("grouped", sp.spmla_sparse_attn_grouped)):
+        times = []
+        for rep in range(args.warmup + args.steps):
+            for b in range(n_bands):
+                a0 = b * w.band
+                bn = min(w.band, w.n_q - a0)
+                d = sp.make_desc(bn, w.q_pos0 + a0, w.window, w.top_k, ratio=w.ratio, band=w.band, n_raw=w.n_raw)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"], sel[a0:a0 + bn].contiguous(),
+                   out[a0:a0 + bn], lse[a0:a0 + bn])
+                e1.record(stream)
+                if rep >= args.warmup:
+                    times.append((e0, e1))
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in times]))
+    bytes_q = attn_bytes_per_query(w)
+    per_launch = float(bytes_q.sum()) / n_bands
+    print(json.dumps({
+        "metric": "attention launch time per 2,048-query band (ms): streaming vs query-tiled",
+        "value": round(res["grouped"], 4), "unit": "ms", "higher_is_better": False,
+        "streaming_ms": round(res["streaming"], 4), "grouped_ms": round(res["grouped"], 4),
+        "grouped_over_streaming": round(res["grouped"] / res["streaming"], 3),
+        "steps": args.steps, "warmup": args.warmup, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "n_q": w.n_q, "top_k": w.top_k, "window": w.window},
+        "model_bytes_per_launch": per_launch,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,8 +197,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--op", choices=["prefill", "compress"], default="prefill",
-                    help="compress: time spmla_compress over the workload's whole raw history")
+    ap.add_argument("--op", choices=["prefill", "compress", "attn-grouped"], default="prefill",
+                    help="compress: time spmla_compress over the workload's whole raw history; "
+                         "attn-grouped: streaming vs query-tiled attention on the same selections")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the prefill bands of one layer fit a single "
@@ -186,6 +230,9 @@ def main():
     sp.load_library()
     if args.op == "compress":
         bench_compress(args, sp, workloads, torch)
+        return
+    if args.op == "attn-grouped":
+        bench_attn_grouped(args, sp, workloads, torch)
         return
     w = workloads.BY_NAME[args.workload]
     log(f"workload {w.name}: generating inputs")

@@ -176,6 +176,20 @@ int spmla_sparse_attn(const spmla_desc* desc, const uint16_t* q, const uint16_t*
                       void* stream);
 
 /*
+ * Query-tiled ("grouped") variant of spmla_sparse_attn (page "perf(ds4):
+ * unify gfx1151 sparse-prefill stack", Validation completed: the streaming
+ * kernel replaced a grouped one, measured side by side). Same arguments,
+ * same results up to fp32 summation order. Each pair of adjacent queries
+ * (t, t+1) shares one gather of the union of their keys: t's selected rows,
+ * t+1's selected rows that t did not select, and the union of the two
+ * windows; every gathered row is read once for both. Selected rows of one
+ * query must be distinct.
+ */
+int spmla_sparse_attn_grouped(const spmla_desc* desc, const uint16_t* q, const uint16_t* kv_comp,
+                              const uint16_t* kv_raw, const int32_t* sel, float* out, float* lse,
+                              void* stream);
+
+/*
  * Ratio-4 compression of raw latent rows: the step before the path (page
  * "perf(ds4): extend sparse prefill scheduling to 10K", Summary: ratio-4
  * compressed rows kept in F16, state committed in chronological order).

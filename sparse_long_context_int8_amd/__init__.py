@@ -25,6 +25,7 @@ __all__ = [
     "spmla_indexer_scores",
     "spmla_topk",
     "spmla_sparse_attn",
+    "spmla_sparse_attn_grouped",
     "spmla_compress",
     "spmla_prefill_workspace_bytes",
     "spmla_prefill",
@@ -49,6 +50,7 @@ EXPORTED_SYMBOLS = [
     "spmla_indexer_scores",
     "spmla_topk",
     "spmla_sparse_attn",
+    "spmla_sparse_attn_grouped",
     "spmla_compress",
     "spmla_prefill_workspace_bytes",
     "spmla_prefill",
@@ -114,6 +116,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spmla_indexer_scores": (ctypes.c_int, [D, P, P, P, P, P]),
         "spmla_topk": (ctypes.c_int, [D, P, P, P, P]),
         "spmla_sparse_attn": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
+        "spmla_sparse_attn_grouped": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
         "spmla_compress": (ctypes.c_int, [D, P, P, ctypes.c_int32, P]),
         "spmla_prefill_workspace_bytes": (ctypes.c_int, [D, ctypes.POINTER(ctypes.c_size_t)]),
         "spmla_prefill": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -193,6 +196,14 @@ def spmla_topk(desc, scores, sel, n_sel=None, stream=None) -> None:
 def spmla_sparse_attn(desc, q, kv_comp, kv_raw, sel, out, lse=None, stream=None) -> None:
     torch = _dt()
     _check(load_library().spmla_sparse_attn(
+        ctypes.byref(desc), _ptr(q, torch.float16, "q"), _ptr(kv_comp, torch.float16, "kv_comp"),
+        _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(sel, torch.int32, "sel"),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def spmla_sparse_attn_grouped(desc, q, kv_comp, kv_raw, sel, out, lse=None, stream=None) -> None:
+    torch = _dt()
+    _check(load_library().spmla_sparse_attn_grouped(
         ctypes.byref(desc), _ptr(q, torch.float16, "q"), _ptr(kv_comp, torch.float16, "kv_comp"),
         _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(sel, torch.int32, "sel"),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))

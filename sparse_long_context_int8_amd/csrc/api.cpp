@@ -210,6 +210,22 @@ int spmla_sparse_attn(const spmla_desc* d, const uint16_t* q, const uint16_t* kv
   return hip_status(spmla::launch_attn(a, (hipStream_t)stream), "attention launch");
 }
 
+int spmla_sparse_attn_grouped(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
+                              const uint16_t* kv_raw, const int32_t* sel, float* out, float* lse,
+                              void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->n_q == 0) return ok();
+  REQUIRE_PTR(q);
+  if (d->n_comp > 0) REQUIRE_PTR(kv_comp);
+  REQUIRE_PTR(kv_raw);
+  REQUIRE_PTR(sel);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(lse);
+  const spmla::AttnArgs a = attn_args(d, q, kv_comp, kv_raw, sel, out, lse);
+  return hip_status(spmla::launch_attn_grouped(a, (hipStream_t)stream), "grouped attention launch");
+}
+
 int spmla_compress(const spmla_desc* d, const uint16_t* kv_raw, uint16_t* kv_comp, int32_t comp_begin,
                    void* stream) {
   int rc = check_desc(d);

@@ -103,6 +103,11 @@ __device__ __forceinline__ short4v lds_read_tr16(unsigned addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
+__device__ __forceinline__ int lds_read_i32(unsigned addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 template <typename T>
 __device__ __forceinline__ void fence_reg(T& v) {
@@ -124,7 +129,6 @@ struct Cfg {
   }
   static constexpr int kNt = (kDv / WAVES) / 16;  // 16-dim output tiles per wave
   static constexpr int kPvSteps = CHUNK / 32;
-  static constexpr int kBLoads = ROPE_REG ? 0 : kRowsPerWave / 8;
   static constexpr int kBufA = CHUNK * 1024;
   static constexpr int kBufB = ROPE_REG ? 0 : CHUNK * 128;
   static constexpr int kBuf = kBufA + kBufB;
@@ -144,47 +148,140 @@ struct Cfg {
 // fp32 sums hold exactly enough, and the O rescale is skipped for most chunks.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int WAVES, int CHUNK, int NBUF, int WPE, bool ROPE_REG>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+// GROUP == 1: streaming, one query per workgroup of WAVES waves.
+// GROUP == 2: query-tiled ("grouped") variant. A workgroup of 2*WAVES waves
+// takes two adjacent queries t0, t1 = t0 + 1 and streams the union of their
+// keys through one set of chunk buffers: t0's selected rows, then t1's
+// selected rows that t0 did not select, then the union of the two windows
+// (raw rows ws0 .. t1). Wave group g (waves g*WAVES ..) runs the streaming
+// per-chunk work for query t_g with its own mask; every gathered row is read
+// once for both queries.
+template <int WAVES, int CHUNK, int NBUF, int WPE, bool ROPE_REG, int GROUP>
+__global__ __launch_bounds__(64 * WAVES * GROUP) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_kernel(AttnArgs a) {
   using C = Cfg<WAVES, CHUNK, NBUF, WPE, ROPE_REG>;
+  static_assert(GROUP == 1 || GROUP == 2, "one or two queries per workgroup");
+  constexpr int kHw = WAVES * GROUP;             // waves in the workgroup
+  constexpr int kRowsPerHw = CHUNK / kHw;        // rows of a chunk each wave gathers
+  constexpr int kRopeLoadsPerHw = (CHUNK / 8 + kHw - 1) / kHw;
+  static_assert(CHUNK % kHw == 0, "gather rows split evenly");
   __shared__ __attribute__((aligned(1024))) char buf0_[C::kBuf];
   __shared__ __attribute__((aligned(1024))) char buf1_[NBUF == 2 ? C::kBuf : 16];
-  __shared__ __attribute__((aligned(16))) float sbuf[NBUF * C::kSBytes / 4];
+  __shared__ __attribute__((aligned(16))) float sbuf[GROUP * NBUF * C::kSBytes / 4];
   lds_char* buf0 = (lds_char*)buf0_;
   lds_char* buf1 = (lds_char*)buf1_;
-  const unsigned sbuf_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)sbuf;
 
-  // Work items (query r, key split s) are dealt to the dies in contiguous
-  // blocks so that the window rows shared by neighbouring queries stay in
-  // one die's L2.
-  const int n_items = a.n_q * a.splits;
+  // Work items (query r, key split s; or a query pair) are dealt to the dies
+  // in contiguous blocks so that the window rows shared by neighbouring
+  // queries stay in one die's L2.
+  const int n_items = GROUP == 1 ? a.n_q * a.splits : (a.n_q + 1) / 2;
   const int per_xcd = (n_items + kXcds - 1) / kXcds;
   const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (item >= n_items) return;
-  const int r = item / a.splits;
-  const int split = item - r * a.splits;
 
-  const int t = a.q_pos0 + r;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = hw % WAVES;  // wave within its group
+  const int grp = hw / WAVES;   // which query of the pair
   const int g = lane >> 4;
   const int c16 = lane & 15;
+  float* sbuf_g = sbuf + grp * NBUF * (C::kSBytes / 4);
+  const unsigned sbuf_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)sbuf_g;
+
+  const int r = GROUP == 1 ? item / a.splits : 2 * item + grp;  // this group's query
+  const int split = GROUP == 1 ? item - r * a.splits : 0;
+  const bool q_valid = r < a.n_q;
+  const int t = a.q_pos0 + (q_valid ? r : r - 1);
 
   const int nv = min(a.n_comp, (t + 1) / a.ratio);
   const int nsel = min(a.top_k, nv);
   const int ws = max(0, t - a.window + 1);
-  const int nk = nsel + (t - ws + 1);
+  // Key list of the workgroup (GROUP == 2: the pair's union, see below).
+  int nk = nsel + (t - ws + 1);
+  int n_a = 0, n_ab = 0, ws0 = 0, t0 = 0, t1 = 0;
+  unsigned list_lds = 0;  // LDS address: t0's selection, then t1's extra rows
+  unsigned bm1_lds = 0;   // LDS address: bitmap of the rows t1 selected
+  bool has1 = false;
+  if constexpr (GROUP == 2) {
+    extern __shared__ int dyn[];  // bitmaps of t0's and t1's rows, then the list
+    const int r0 = 2 * item;
+    has1 = r0 + 1 < a.n_q;
+    t0 = a.q_pos0 + r0;
+    t1 = t0 + 1;
+    const int nv0 = min(a.n_comp, (t0 + 1) / a.ratio);
+    const int nv1 = has1 ? min(a.n_comp, (t1 + 1) / a.ratio) : 0;
+    n_a = min(a.top_k, nv0);
+    const int n_s1 = has1 ? min(a.top_k, nv1) : 0;
+    ws0 = max(0, t0 - a.window + 1);
+    const int words = (a.n_comp + 31) / 32;
+    unsigned* b0 = reinterpret_cast<unsigned*>(dyn);
+    unsigned* b1 = b0 + words;
+    int* lst = reinterpret_cast<int*>(b1 + words);
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 2 * words; i += 64 * kHw) b0[i] = 0u;
+    __syncthreads();
+    const int32_t* s0 = a.sel + (int64_t)r0 * a.top_k;
+    const int32_t* s1 = a.sel + (int64_t)(r0 + 1) * a.top_k;
+    for (int i = tid; i < n_a; i += 64 * kHw) {
+      const int idx = s0[i];
+      lst[i] = idx;
+      if (idx >= 0 && idx < nv0) atomicOr(&b0[idx >> 5], 1u << (idx & 31));
+    }
+    for (int i = tid; i < n_s1; i += 64 * kHw) {
+      const int idx = s1[i];
+      if (idx >= 0 && idx < nv1) atomicOr(&b1[idx >> 5], 1u << (idx & 31));
+    }
+    __syncthreads();
+    // t1's valid rows that t0 did not select, in t1's order: a block-wide
+    // exclusive scan over consecutive runs of its list (deterministic).
+    __shared__ int wsum[kHw];
+    const int per = (n_s1 + 64 * kHw - 1) / (64 * kHw);
+    int take = 0;
+    for (int u = 0; u < per; ++u) {
+      const int i = tid * per + u;
+      if (i < n_s1) {
+        const int idx = s1[i];
+        take += (idx >= 0 && idx < nv1 && !((b0[idx >> 5] >> (idx & 31)) & 1u)) ? 1 : 0;
+      }
+    }
+    int incl = take;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[hw] = incl;
+    __syncthreads();
+    int pos = n_a + incl - take, n_b = 0;
+    for (int w = 0; w < kHw; ++w) {
+      pos += w < hw ? wsum[w] : 0;
+      n_b += wsum[w];
+    }
+    for (int u = 0; u < per; ++u) {
+      const int i = tid * per + u;
+      if (i < n_s1) {
+        const int idx = s1[i];
+        if (idx >= 0 && idx < nv1 && !((b0[idx >> 5] >> (idx & 31)) & 1u)) lst[pos++] = idx;
+      }
+    }
+    __syncthreads();
+    n_ab = n_a + n_b;
+    nk = n_ab + ((has1 ? t1 : t0) - ws0 + 1);
+    const unsigned dyn_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)dyn;
+    bm1_lds = dyn_lds + 4u * words;
+    list_lds = dyn_lds + 8u * words;
+  }
   const int nchunks = (nk + CHUNK - 1) / CHUNK;
   // This work item's chunks [c_begin, c_end) of the query's key list.
   const int per_split = (nchunks + a.splits - 1) / a.splits;
   const int c_begin = split * per_split;
   const int c_end = min(nchunks, c_begin + per_split);
-  const int32_t* sel_row = a.sel + (int64_t)r * a.top_k;
+  const int32_t* sel_row = a.sel + (int64_t)(q_valid ? r : r - 1) * a.top_k;
   const char* comp_base = reinterpret_cast<const char*>(a.kv_comp);
   const char* raw_base = reinterpret_cast<const char*>(a.kv_raw);
   const char* self_row = raw_base + (int64_t)t * kRowBytes;
 
+  (void)has1;
   // QK work item of this wave: key tile and contraction slice.
   const int tile = wave % C::kTiles;
   const int half = wave / C::kTiles;
@@ -197,35 +294,62 @@ void attn_kernel(AttnArgs a) {
   float m_ref = -__builtin_inff();  // softmax reference (log2 domain) of head c16
   float l_run = 0.f;                // this lane's share of the softmax sum
 
-  // Selected index of key k0 + lane: one in-bounds load per call.
+  // Selected index of key k0 + lane: one in-bounds load per call (the pair
+  // variant reads its list from LDS in row_of instead).
   auto load_sel = [&](int ch) -> int {
+    if constexpr (GROUP == 2) return 0;
     const int key = min(ch * CHUNK + lane, a.top_k - 1);
     return __builtin_nontemporal_load(sel_row + key);
   };
-  // Row pointer and validity of key k0 + lane.
+  // Row pointer of key k0 + lane, and whether this group's query uses it.
   auto row_of = [&](int ch, int selv, bool& ok) -> const char* {
     const int key = ch * CHUNK + lane;
     ok = false;
     const char* p = self_row;
-    if (key < nsel) {
-      ok = (selv >= 0) && (selv < nv);
-      if (ok) p = comp_base + (int64_t)selv * kRowBytes;
-    } else if (key < nk) {
-      ok = true;
-      p = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
+    if constexpr (GROUP == 1) {
+      if (key < nsel) {
+        ok = (selv >= 0) && (selv < nv);
+        if (ok) p = comp_base + (int64_t)selv * kRowBytes;
+      } else if (key < nk) {
+        ok = true;
+        p = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
+      }
+    } else {
+      if (key < n_ab) {
+        const int idx = lds_read_i32(list_lds + 4u * key);
+        lds_wait();
+        const bool in_range = idx >= 0 && idx < a.n_comp;
+        if (in_range) p = comp_base + (int64_t)idx * kRowBytes;
+        if (key < n_a) {  // t0's own selection
+          const bool ok0 = idx >= 0 && idx < nv;  // grp 0: nv is t0's
+          if (grp == 0) {
+            ok = ok0;
+          } else if (in_range && has1) {
+            const unsigned word = (unsigned)lds_read_i32(bm1_lds + 4u * (idx >> 5));
+            lds_wait();
+            ok = (word >> (idx & 31)) & 1u;
+          }
+        } else {  // rows only t1 selected
+          ok = grp == 1;
+        }
+      } else if (key < nk) {
+        const int srow = ws0 + (key - n_ab);
+        p = raw_base + (int64_t)srow * kRowBytes;
+        ok = srow >= ws && srow <= t && q_valid;
+      }
     }
     return p;
   };
   // This wave's share of the gather of one chunk, plus (rope in registers)
   // the rope fragments of the rows this wave scores.
-  const int row0 = wave * C::kRowsPerWave;
+  const int row0 = hw * kRowsPerHw;
   auto gather = [&](const char* kp, lds_char* buf, half8 (&rope)[2]) {
     lds_char* bufA = buf;
     const uintptr_t kpi = (uintptr_t)kp;
     const unsigned kp_lo = (unsigned)kpi;
     const unsigned kp_hi = (unsigned)(kpi >> 32);
 #pragma unroll
-    for (int i = 0; i < C::kRowsPerWave; ++i) {
+    for (int i = 0; i < kRowsPerHw; ++i) {
       const int n = row0 + i;
       const unsigned lo = __builtin_amdgcn_readlane(kp_lo, n);
       const unsigned hi = __builtin_amdgcn_readlane(kp_hi, n);
@@ -235,14 +359,18 @@ void attn_kernel(AttnArgs a) {
     }
     if constexpr (!ROPE_REG) {
       lds_char* bufB = bufA + C::kBufA;
+      // Rope load j covers rows 8j .. 8j+7; they are dealt to the waves.
 #pragma unroll
-      for (int j = 0; j < C::kBLoads; ++j) {
-        const int nb = row0 + 8 * j + (lane >> 3);
-        const unsigned lo = __shfl(kp_lo, nb);
-        const unsigned hi = __shfl(kp_hi, nb);
-        const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
-        const int off = (64 + ((lane & 7) ^ swz_b(nb))) << 4;
-        __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), bufB + (row0 + 8 * j) * 128, 16, 0, 0);
+      for (int jj = 0; jj < kRopeLoadsPerHw; ++jj) {
+        const int j = hw + jj * kHw;
+        if (j < CHUNK / 8) {
+          const int nb = 8 * j + (lane >> 3);
+          const unsigned lo = __shfl(kp_lo, nb);
+          const unsigned hi = __shfl(kp_hi, nb);
+          const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
+          const int off = (64 + ((lane & 7) ^ swz_b(nb))) << 4;
+          __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), bufB + 8 * j * 128, 16, 0, 0);
+        }
       }
     } else {
       if (has_rope) {
@@ -263,7 +391,7 @@ void attn_kernel(AttnArgs a) {
   // last read of it.
   auto compute = [&](lds_char* cur, unsigned long long valid, const half8 (&rope)[2], int sb) {
     const unsigned bA = (unsigned)(uintptr_t)cur;  // LDS byte address
-    float* sbuf_c = sbuf + sb * (C::kSBytes / 4);
+    float* sbuf_c = sbuf_g + sb * (C::kSBytes / 4);
     const unsigned sbuf_c_addr = sbuf_addr + sb * C::kSBytes;
     // The contraction slice is a compile-time constant inside qk(), so each
     // K read address is fixed at compile time (no per-read branches).
@@ -440,7 +568,7 @@ void attn_kernel(AttnArgs a) {
     gather(kp0, buf0, rope_cur);
   }
   {
-    const _Float16* qrow = a.q + ((int64_t)r * kHeads + c16) * kDqk + 8 * g;
+    const _Float16* qrow = a.q + ((int64_t)(q_valid ? r : r - 1) * kHeads + c16) * kDqk + 8 * g;
     const int q_start = C::start(half), q_len = C::len(half);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
@@ -503,6 +631,7 @@ void attn_kernel(AttnArgs a) {
     }
     return;
   }
+  if (!q_valid) return;  // the pair's missing second query
   const float inv = 1.0f / l_tot;
   float* orow = a.out + ((int64_t)r * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
 #pragma unroll
@@ -603,11 +732,26 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
   const int per_xcd = (a.n_q * a.splits + kXcds - 1) / kXcds;
   constexpr int W = SPMLA_ATTN_WAVES;
   hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE,
-                                  (bool)SPMLA_ATTN_ROPE_REG>),
+                                  (bool)SPMLA_ATTN_ROPE_REG, 1>),
                      dim3(per_xcd * kXcds), dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_q * kHeads), dim3(kDv / 4), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_grouped(const AttnArgs& a_in, hipStream_t stream) {
+  if (a_in.n_q <= 0) return hipSuccess;
+  AttnArgs a = a_in;
+  a.splits = 1;
+  const int pairs = (a.n_q + 1) / 2;
+  const int per_xcd = (pairs + kXcds - 1) / kXcds;
+  // Bitmaps of the two queries' rows and the pair's row list.
+  const size_t words = ((size_t)a.n_comp + 31) / 32;
+  const size_t lds = 4 * (2 * words + 2 * (size_t)a.top_k);
+  hipLaunchKernelGGL((attn_kernel<SPMLA_ATTN_WAVES, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE,
+                                  (bool)SPMLA_ATTN_ROPE_REG, 2>),
+                     dim3(per_xcd * kXcds), dim3(128 * SPMLA_ATTN_WAVES), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -126,6 +126,9 @@ hipError_t launch_fused_topk(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_sample_threshold(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_collect(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+// Query-tiled variant: pairs of adjacent queries share one gather of their
+// key union (same results as launch_attn up to fp32 summation order).
+hipError_t launch_attn_grouped(const AttnArgs& a, hipStream_t stream);
 // kv_comp rows comp_begin .. n_comp-1 from kv_raw (ratio 4, d_qk wide).
 hipError_t launch_compress(const uint16_t* kv_raw, uint16_t* kv_comp, int comp_begin, int n_comp,
                            hipStream_t stream);

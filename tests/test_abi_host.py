@@ -136,6 +136,7 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
         assert "aligned" in lib.spmla_last_error().decode()
     assert _call_prefill(lib, d, good, 0) == sp.SPMLA_EWORKSPACE
     assert lib.spmla_sparse_attn(ctypes.byref(d), None, None, None, None, None, None, None) == sp.SPMLA_EINVAL
+    assert lib.spmla_sparse_attn_grouped(ctypes.byref(d), None, None, None, None, None, None, None) == sp.SPMLA_EINVAL
     assert lib.spmla_topk(ctypes.byref(d), None, None, None, None) == sp.SPMLA_EINVAL
     assert lib.spmla_indexer_scores(ctypes.byref(d), None, None, None, None, None) == sp.SPMLA_EINVAL
     assert lib.spmla_check_desc(None) == sp.SPMLA_EINVAL

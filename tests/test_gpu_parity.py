@@ -197,6 +197,62 @@ def test_key_splits_match_whole_queries(sp):
     assert_close(l_sub.cpu().numpy()[rows], np.concatenate([r_["lse"] for r_ in ref]), "splits lse vs oracle")
 
 
+GROUPED = [
+    ("tiny-256", workloads.TINY_256, None),
+    ("band-2048", workloads.BAND_2048, None),
+    ("odd-count-long-history", workloads.LayerShape("g1", n_q=37, q_pos0=120000, window=128, top_k=2048), 9),
+    ("ragged", workloads.LayerShape("g2", n_q=133, q_pos0=61, window=7, top_k=17), 10),
+]
+
+
+@pytest.mark.parametrize("name,w,seed", GROUPED, ids=[g[0] for g in GROUPED])
+def test_grouped_attention_matches_oracle(sp, name, w, seed):
+    """The query-tiled variant on the oracle's own selections: every query's
+    output within tolerance (odd query counts leave the last pair half)."""
+    import torch
+
+    say(f"[parity grouped] {name}")
+    x = workloads.generate(w, seed=seed)
+    dev = to_dev(x)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    sel = torch.from_numpy(ref["sel"]).cuda()
+    out = torch.empty((w.n_q, 16, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.n_q, 16), dtype=torch.float32, device="cuda")
+    sp.spmla_sparse_attn_grouped(desc_of(sp, w), dev["q"], dev["kv_comp"], dev["kv_raw"], sel, out, lse)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref["out"], f"grouped {name} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"grouped {name} lse")
+
+
+def test_grouped_attention_full_size_sampled(sp):
+    """prefill-8192's last band with the GPU's own selections: grouped against
+    streaming on every query, and against the oracle on sampled queries."""
+    import torch
+
+    w = workloads.PREFILL_8192
+    say("[parity grouped] prefill-8192 last band")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    _, _, sel = sp.prefill(desc_of(sp, w), dev)
+    a0, n = 6144, 2048
+    d = sp.make_desc(n, a0, w.window, w.top_k, n_raw=w.n_raw)
+    qs, ss = dev["q"][a0:], sel[a0:].contiguous()
+    o_s = torch.empty((n, 16, 512), dtype=torch.float32, device="cuda")
+    o_g = torch.empty_like(o_s)
+    sp.spmla_sparse_attn(d, qs, dev["kv_comp"], dev["kv_raw"], ss, o_s, None)
+    sp.spmla_sparse_attn_grouped(d, qs, dev["kv_comp"], dev["kv_raw"], ss, o_g, None)
+    torch.cuda.synchronize()
+    assert_close(o_g.cpu().numpy(), o_s.cpu().numpy().astype(np.float64), "grouped vs streaming")
+    rows = [0, 1, 2, 1001, 2046, 2047]
+    got, want = [], []
+    for r in rows:
+        ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k, scale=w.scale,
+                             d_v=w.d_v, q_begin=a0 + r, q_end=a0 + r + 1)
+        got.append(o_g[r].cpu().numpy()), want.append(ref["out"][0])
+    assert_close(np.array(got), np.array(want), "grouped vs oracle")
+
+
 # ------------------------------------------------------------- properties
 def test_deterministic_and_band_invariant(sp):
     import torch
