@@ -114,6 +114,25 @@ def test_workspace_bytes():
     assert nb4 >= 2048 * 30719 * 4 + 2048 * 2048 * 4
 
 
+def test_workspace_covers_split_partials_and_fused_candidates():
+    """Small calls need room for the attention's key-split partials (up to
+    64 splits x [16][512] + (m, l) per query); long-history bands need the
+    fused selection's slots; both fit the scratch the call reports."""
+    per_split = (16 * 512 + 16 * 2) * 4
+    for w in (workloads.DECODE_1, workloads.VERIFY_5):
+        nb = sp.spmla_prefill_workspace_bytes(desc_of(w))
+        splits = min(64, -(-1024 // w.n_q))
+        assert nb >= w.n_q * splits * per_split
+    d = sp.make_desc(300, 6000, 128, 512)  # 300 queries: 4 splits each
+    assert sp.spmla_prefill_workspace_bytes(d) >= 300 * 4 * per_split
+    w = workloads.CHUNK_8192_AT_114687
+    nb = sp.spmla_prefill_workspace_bytes(desc_of(w))
+    n_spans = -(-w.n_comp // 512)
+    assert nb >= 2048 * n_spans * 128 * 8 + 2048 * n_spans * 4  # candidate slots + counts
+    # a call too large for splits needs no partials: the dense band dominates
+    assert sp.spmla_prefill_workspace_bytes(desc_of(workloads.PREFILL_8192)) == 2048 * 2048 * 4 + 2048 * 512 * 4
+
+
 A = 1 << 20  # an aligned fake address; never dereferenced by these calls
 
 
