@@ -17,7 +17,7 @@ fp64. Every function follows one step of the method as the pages state it:
     FP32-staged streaming attention with a softmax (accuracy reported as NMSE
     and max-abs error against a precise path).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * indexer score S[t,j] = sum_h w[t,h] * max(0, <iq[t,h,:], ik[j,:]>): the
     DeepSeek sparse-attention indexer form; the pages never print it, so this
     formula is "parity unpinned" by the pages (its implementation is pinned by
