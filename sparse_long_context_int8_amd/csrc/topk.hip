@@ -16,10 +16,14 @@
 //      atomic contention low for bell-shaped score distributions);
 //   2. refinement: MSD radix select over the remaining key bits, only for
 //      the rows in that bin (usually a handful);
-//   3. ordering: the winners are bucketed by the top 11 bits of their key
-//      offset, bucket offsets come from one prefix scan, and each winner's
+//   3. ordering: the collected keys are bucketed by the top 11 bits of their
+//      offset, bucket offsets come from one prefix scan, and each key's
 //      place inside its bucket is the number of larger keys in the bucket
-//      (buckets hold a few keys for spread-out scores).
+//      (buckets hold a few keys for spread-out scores); the first k places
+//      are the output.
+// The refinement (2) runs only while the keys at or above the threshold
+// would exceed k + 512; usually the coarse bin already gets there, and its
+// extra keys simply fall beyond place k.
 // Integer only: exact, and independent of thread timing.
 #include "spmla_internal.h"
 
@@ -30,6 +34,7 @@ typedef unsigned long long u64;
 
 constexpr int kBins1 = 2048;  // coarse-pass and ordering bins (11 bits)
 constexpr int kBits1 = 11;
+constexpr int kSlack = 512;  // elements beyond k a workgroup may collect and order
 
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
@@ -87,6 +92,32 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, i
   __syncthreads();
 }
 
+// Bucket offsets, largest bucket first: boff[b] = elements in buckets above
+// b; hist[] (the counts) becomes the fill cursor of each bucket. Ends with a
+// barrier.
+template <int BLOCK>
+__device__ __forceinline__ void bucket_offsets(int* hist, int* boff, int* red) {
+  constexpr int kPer = kBins1 / BLOCK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) tot += hist[kBins1 - 1 - (tid * kPer + i)];
+  const int incl = wave_incl_scan(tot, lane);
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  int base = incl - tot;
+  for (int w = 0; w < wave; ++w) base += red[w];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kBins1 - 1 - (tid * kPer + i);
+    const int c = hist[b];
+    boff[b] = base;
+    hist[b] = base;
+    base += c;
+  }
+  __syncthreads();
+}
+
 // Where a workgroup's elements come from.
 enum Src : int {
   kDense = 0,      // row r of the score matrix: element e is row e
@@ -94,8 +125,8 @@ enum Src : int {
   kRecompute = 2,  // scores recomputed from the indexer inputs (listed tokens)
 };
 
-// Selection and ordering for token r of the launch. LDS: `keys` holds
-// 2 * top_k keys (winners, then their bucketed copy).
+// Selection and ordering for token r of the launch. LDS: `keys` holds twice
+// min(top_k + kSlack, BLOCK * PER) keys (collected, then their bucketed copy).
 template <int BLOCK, int PER, int SRC>
 __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f, int r) {
   constexpr int NW = BLOCK / 64;
@@ -246,8 +277,13 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     return (s << ebits) | (u64)(nv - 1 - j);
   };
 
-  u64 thresh = 0;  // selected iff key >= thresh
-  if (n_el > nsel) {  // then nsel == k
+  // Elements with key >= thresh are collected and ordered, the first nsel
+  // places kept. The threshold only has to leave at most `cap` of them and
+  // keep every winner: the coarse bin holding the k-th key usually does, so
+  // the refinement below only runs when that bin is crowded (heavy ties).
+  const int cap = min(k + kSlack, BLOCK * PER);  // n_el <= BLOCK * PER
+  u64 thresh = 0;
+  if (n_el > cap) {
     // 1. coarse pass on the top kBits1 bits of (score - min).
     const int sh1 = sbits > kBits1 ? sbits - kBits1 : 0;
     for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
@@ -263,7 +299,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     int need = k - s_above;
     const int low_bits = sh1 + ebits;  // key bits below the coarse digit
     u64 prefix = (u64)bin1;            // key >> shift must equal this
-    if (s_count == need || low_bits == 0) {
+    if (s_above + s_count <= cap || low_bits == 0) {
       thresh = prefix << low_bits;
     } else {
       // 2. refine inside the bin with 8-bit digits of the remaining bits.
@@ -289,7 +325,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
         need -= s_above;
         prefix = (prefix << dbits) | (u64)s_bin;
         top = shift;
-        if (s_count == need || shift == 0) {
+        if ((k - need) + s_count <= cap || shift == 0) {
           thresh = prefix << shift;
           break;
         }
@@ -298,10 +334,10 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     }
   }
 
-  // 3. Collect the nsel winners into keys[0 .. nsel) (one LDS atomic per
-  // wave and register, lanes take consecutive slots) and count them per
-  // ordering bucket: the top 11 bits of (key - thresh); no winner key
-  // exceeds key_hi.
+  // 3. Collect the elements >= thresh (at most cap, at least nsel) into
+  // keys[0 ..) (one LDS atomic per wave and register, lanes take consecutive
+  // slots) and count them per ordering bucket: the top 11 bits of
+  // (key - thresh); no key exceeds key_hi.
   const u64 key_hi = ((u64)span << ebits) | emask;
   const u64 kspan = key_hi - thresh;
   const int kbits = kspan ? 64 - __clzll(kspan) : 0;
@@ -321,7 +357,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     if (lane == 0) base = atomicAdd(&s_cnt, __popcll(m));
     base = __shfl(base, 0);
     const int pos = base + __popcll(m & below);
-    if (take && pos < k) {  // pos < nsel <= k by construction
+    if (take && pos < cap) {  // pos < cap by construction
       const u64 key = key_of(i);
       keys[pos] = key;
       atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
@@ -329,42 +365,23 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   }
   __syncthreads();
 
-  // Bucket offsets, largest bucket first: boff[b] = winners in buckets > b;
-  // hist[] becomes the fill cursor of each bucket.
-  {
-    constexpr int kPer = kBins1 / BLOCK;
-    int tot = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) tot += hist[kBins1 - 1 - (tid * kPer + i)];
-    const int incl = wave_incl_scan(tot, lane);
-    if (lane == 63) red_c[wave] = incl;
-    __syncthreads();
-    int base = incl - tot;
-    for (int w = 0; w < wave; ++w) base += red_c[w];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int b = kBins1 - 1 - (tid * kPer + i);
-      const int c = hist[b];
-      boff[b] = base;
-      hist[b] = base;
-      base += c;
-    }
-  }
-  __syncthreads();
-  u64* bucketed = keys + k;
-  for (int e = tid; e < nsel; e += BLOCK) {
+  bucket_offsets<BLOCK>(hist, boff, red_c);
+  const int n_coll = min(s_cnt, cap);
+  u64* bucketed = keys + cap;
+  for (int e = tid; e < n_coll; e += BLOCK) {
     const u64 key = keys[e];
     bucketed[atomicAdd(&hist[(int)((key - thresh) >> shb)], 1)] = key;
   }
   __syncthreads();
-  // Place of a winner = its bucket's offset + larger keys in the bucket.
-  for (int p = tid; p < nsel; p += BLOCK) {
+  // Place of an element = its bucket's offset + larger keys in the bucket;
+  // the first nsel places are the selection, in order.
+  for (int p = tid; p < n_coll; p += BLOCK) {
     const u64 key = bucketed[p];
     const int b = (int)((key - thresh) >> shb);
     const int st = boff[b], en = hist[b];
-    int rank = 0;
-    for (int q = st; q < en; ++q) rank += bucketed[q] > key ? 1 : 0;
-    sel_row[st + rank] = (nv - 1) - (int)(key & emask);
+    int place = st;
+    for (int q = st; q < en; ++q) place += bucketed[q] > key ? 1 : 0;
+    if (place < nsel) sel_row[place] = (nv - 1) - (int)(key & emask);
   }
   for (int i = nsel + tid; i < k; i += BLOCK) sel_row[i] = -1;
   if (a.n_sel && tid == 0) a.n_sel[r] = nsel;
@@ -387,8 +404,8 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a, FusedArgs f) {
 
 template <int BLOCK, int PER, int SRC>
 hipError_t launch_cfg(const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
-  // keys: the winners and their bucketed copy.
-  const size_t lds = 2 * sizeof(u64) * (size_t)a.top_k;
+  // keys: the collected elements (at most top_k + kSlack) and their bucketed copy.
+  const size_t lds = 2 * sizeof(u64) * (size_t)std::min(a.top_k + kSlack, BLOCK * PER);
   hipLaunchKernelGGL((topk_kernel<BLOCK, PER, SRC>), dim3(grid), dim3(BLOCK), lds, stream, a, f);
   return hipGetLastError();
 }
