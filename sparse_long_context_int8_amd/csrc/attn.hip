@@ -108,15 +108,21 @@ __device__ __forceinline__ int lds_read_i32(unsigned addr) {
   asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
+__device__ __forceinline__ unsigned long long lds_read_u64(unsigned addr) {
+  unsigned long long v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 template <typename T>
 __device__ __forceinline__ void fence_reg(T& v) {
   asm volatile("" : "+v"(v));
 }
 
-template <int WAVES, int CHUNK, int NBUF, int WPE, bool ROPE_REG>
+template <int WAVES, int CHUNK, int NBUF, int WPE, int GROUP>
 struct Cfg {
-  static constexpr int kRowsPerWave = CHUNK / WAVES;
+  static constexpr int kHw = WAVES * GROUP;       // waves in the workgroup
+  static constexpr int kRowsPerHw = CHUNK / kHw;  // rows of a chunk each wave gathers
   static constexpr int kTiles = CHUNK / 16;
   static constexpr int kHalves = WAVES / kTiles;  // slices of the 576 contraction
   // Slice h covers k-steps [start(h), start(h) + len(h)) of the 18 steps of
@@ -128,48 +134,116 @@ struct Cfg {
     return h * (kAllSteps / kHalves) + (h < kAllSteps % kHalves ? h : kAllSteps % kHalves);
   }
   static constexpr int kNt = (kDv / WAVES) / 16;  // 16-dim output tiles per wave
-  static constexpr int kPvSteps = CHUNK / 32;
+  // PV steps: 32 keys (16x16x32 MFMA) or, for 16-key chunks, 16 keys
+  // (16x16x16 MFMA); each lane holds kKpl keys of one head per step.
+  static constexpr int kPvKeys = CHUNK >= 32 ? 32 : 16;
+  static constexpr int kPvSteps = CHUNK / kPvKeys;
+  static constexpr int kKpl = kPvKeys / 4;
+  static constexpr int kUnits = kKpl / 4;  // 16-byte S^T units (and V^T reads) per lane and PV step
   static constexpr int kBufA = CHUNK * 1024;
-  static constexpr int kBufB = ROPE_REG ? 0 : CHUNK * 128;
+  static constexpr int kBufB = CHUNK * 128;
   static constexpr int kBuf = kBufA + kBufB;
   static constexpr int kSStride = CHUNK;  // floats per head row of S^T partials
   static constexpr int kSBytes = kHalves * kHeads * kSStride * 4;
-  static constexpr int kLds = NBUF * (kBuf + kSBytes);
-  // k-steps 16 and 17 (the rope dims) belong to the last contraction slice.
+  static constexpr int kSBufs = GROUP == 1 ? 1 : 2;  // S^T exchange areas per query
+  // Streaming (GROUP == 1): selected indices and validity masks of the
+  // chunks in flight, slot = chunk mod kSlots.
+  static constexpr int kSlots = GROUP == 1 ? 2 * NBUF + 2 : 1;
+  static constexpr int kLds = NBUF * kBuf + GROUP * kSBufs * kSBytes + kSlots * (4 * CHUNK + 8);
+  // Global->LDS loads a wave issues per chunk: its rows, one rope load, and
+  // (streaming) the selected indices of a later chunk.
+  static constexpr int kOpsPerChunk = kRowsPerHw + 2;
+  static constexpr int kWaitAhead = 1 + (NBUF - 1) * kOpsPerChunk;
   static_assert(kTiles * kHalves == WAVES, "QK work must split evenly");
-  static_assert(ROPE_REG || kRowsPerWave % 8 == 0, "rope loads cover 8 rows");
+  static_assert(CHUNK % kHw == 0 && kRowsPerHw <= 8, "gather rows split evenly, one rope load per wave");
   static_assert(start(kHalves - 1) <= 16, "rope steps live in the last slice");
-  static_assert(CHUNK % 32 == 0, "PV steps are 32 keys");
-  static_assert(kLds * ((WPE * 4) / WAVES) <= 160 * 1024, "LDS for the requested occupancy");
+  static_assert(CHUNK == 16 || CHUNK % 32 == 0, "PV steps are 16 or 32 keys");
+  static_assert(CHUNK <= 64, "validity is one 64-bit mask per chunk");
+  static_assert(GROUP == 1 || NBUF == 2, "the pair variant double-buffers");
+  static_assert(NBUF >= 2 && kWaitAhead < 64, "vmcnt range");
+  static_assert(kLds * ((WPE * 4) / kHw) <= 160 * 1024, "LDS for the requested occupancy");
 };
+
+// S^T exchange slot (16-byte unit of a head row) of key unit u (keys
+// 4u .. 4u+3) for head h: rows of 32 keys XOR (h1, h0, h2), rows of 16 keys
+// XOR (h1, h2), so that the 8 lanes of one 16-byte access phase hit
+// distinct banks.
+template <int CHUNK>
+__device__ __forceinline__ int s_slot(int u, int h) {
+  if constexpr (CHUNK == 16) return u ^ ((h >> 1) & 3);
+  return u ^ swz_s(h);
+}
+
+// Calls f(integral_constant<int, h>) for the runtime slice index h < N
+// (wave-uniform), so that each slice's LDS addresses are compile-time.
+template <int N, typename F>
+__device__ __forceinline__ void with_slice(int h, F&& f) {
+  if constexpr (N == 1) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (h == N - 1) f(std::integral_constant<int, N - 1>{});
+    else with_slice<N - 1>(h, f);
+  }
+}
+
+// Max and sum over the four lanes l, l^16, l^32, l^48 (one head's keys)
+// with the gfx950 row swaps: a swap of a value with itself leaves, in its
+// two results, the value of lane l and of its partner lane.
+__device__ __forceinline__ unsigned fbits(float v) { return __builtin_bit_cast(unsigned, v); }
+__device__ __forceinline__ float ffrom(unsigned v) { return __builtin_bit_cast(float, v); }
+__device__ __forceinline__ float max4_heads(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  const float m = fmaxf(ffrom(a[0]), ffrom(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(fbits(m), fbits(m), false, false);
+  return fmaxf(ffrom(b[0]), ffrom(b[1]));
+}
+__device__ __forceinline__ float sum4_heads(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  const float m = ffrom(a[0]) + ffrom(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(fbits(m), fbits(m), false, false);
+  return ffrom(b[0]) + ffrom(b[1]);
+}
 
 // Softmax reference is moved only when a chunk's max exceeds it by more than
 // this (log2 units); probabilities are then at most 2^8, which fp16 P and
 // fp32 sums hold exactly enough, and the O rescale is skipped for most chunks.
 constexpr float kRescaleThreshold = 8.0f;
 
-// GROUP == 1: streaming, one query per workgroup of WAVES waves.
+// GROUP == 1: streaming, one (query, key split) per workgroup of WAVES
+// waves, keys through a ring of NBUF chunk buffers. A chunk's buffer is read
+// (K and V^T fragments into registers) before its S^T exchange barrier; right
+// after that barrier the gather of the chunk NBUF places later is issued into
+// it, so NBUF gathers are in flight while softmax and PV run. The selected
+// indices arrive by the same global->LDS path ahead of their gather, so the
+// loop issues no other global load and each wave's only memory wait is a
+// vmcnt that lets the later chunks' loads stay outstanding (loads complete
+// in issue order).
 // GROUP == 2: query-tiled ("grouped") variant. A workgroup of 2*WAVES waves
 // takes two adjacent queries t0, t1 = t0 + 1 and streams the union of their
-// keys through one set of chunk buffers: t0's selected rows, then t1's
-// selected rows that t0 did not select, then the union of the two windows
-// (raw rows ws0 .. t1). Wave group g (waves g*WAVES ..) runs the streaming
-// per-chunk work for query t_g with its own mask; every gathered row is read
-// once for both queries.
-template <int WAVES, int CHUNK, int NBUF, int WPE, bool ROPE_REG, int GROUP>
+// keys through two chunk buffers: t0's selected rows, then t1's selected
+// rows that t0 did not select, then the union of the two windows (raw rows
+// ws0 .. t1). Wave group g (waves g*WAVES ..) runs the streaming per-chunk
+// work for query t_g with its own mask; every gathered row is read once for
+// both queries.
+template <int WAVES, int CHUNK, int NBUF, int WPE, int GROUP>
 __global__ __launch_bounds__(64 * WAVES * GROUP) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_kernel(AttnArgs a) {
-  using C = Cfg<WAVES, CHUNK, NBUF, WPE, ROPE_REG>;
+  using C = Cfg<WAVES, CHUNK, NBUF, WPE, GROUP>;
   static_assert(GROUP == 1 || GROUP == 2, "one or two queries per workgroup");
-  constexpr int kHw = WAVES * GROUP;             // waves in the workgroup
-  constexpr int kRowsPerHw = CHUNK / kHw;        // rows of a chunk each wave gathers
-  constexpr int kRopeLoadsPerHw = (CHUNK / 8 + kHw - 1) / kHw;
-  static_assert(CHUNK % kHw == 0, "gather rows split evenly");
-  __shared__ __attribute__((aligned(1024))) char buf0_[C::kBuf];
-  __shared__ __attribute__((aligned(1024))) char buf1_[NBUF == 2 ? C::kBuf : 16];
-  __shared__ __attribute__((aligned(16))) float sbuf[GROUP * NBUF * C::kSBytes / 4];
-  lds_char* buf0 = (lds_char*)buf0_;
-  lds_char* buf1 = (lds_char*)buf1_;
+  constexpr int kHw = C::kHw;
+  constexpr int kRowsPerHw = C::kRowsPerHw;
+  constexpr int kKpl = C::kKpl;
+  constexpr int kUnits = C::kUnits;
+  __shared__ __attribute__((aligned(1024))) char bufs_[NBUF * C::kBuf];
+  __shared__ __attribute__((aligned(16))) float sbuf[GROUP * C::kSBufs * C::kSBytes / 4];
+  __shared__ __attribute__((aligned(16))) int sel_ring[C::kSlots * CHUNK];
+  __shared__ unsigned long long valid_ring[C::kSlots];
+  // Lambdas below use these pointers, never the __shared__ arrays by name.
+  lds_char* const bufs = (lds_char*)bufs_;
+  lds_char* const sel_lds = (lds_char*)sel_ring;
+  unsigned long long* const valid_slots = valid_ring;
+  const unsigned sel_ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)sel_ring;
+  const unsigned valid_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned long long*)valid_ring;
 
   // Work items (query r, key split s; or a query pair) are dealt to the dies
   // in contiguous blocks so that the window rows shared by neighbouring
@@ -185,7 +259,7 @@ void attn_kernel(AttnArgs a) {
   const int grp = hw / WAVES;   // which query of the pair
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  float* sbuf_g = sbuf + grp * NBUF * (C::kSBytes / 4);
+  float* sbuf_g = sbuf + grp * C::kSBufs * (C::kSBytes / 4);
   const unsigned sbuf_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)sbuf_g;
 
   const int r = GROUP == 1 ? item / a.splits : 2 * item + grp;  // this group's query
@@ -285,7 +359,6 @@ void attn_kernel(AttnArgs a) {
   // QK work item of this wave: key tile and contraction slice.
   const int tile = wave % C::kTiles;
   const int half = wave / C::kTiles;
-  const bool has_rope = ROPE_REG && half == C::kHalves - 1;
 
   half8 qf[C::kSteps];
   float4v acc_o[C::kNt];
@@ -294,57 +367,69 @@ void attn_kernel(AttnArgs a) {
   float m_ref = -__builtin_inff();  // softmax reference (log2 domain) of head c16
   float l_run = 0.f;                // this lane's share of the softmax sum
 
-  // Selected index of key k0 + lane: one in-bounds load per call (the pair
-  // variant reads its list from LDS in row_of instead).
-  auto load_sel = [&](int ch) -> int {
-    if constexpr (GROUP == 2) return 0;
-    const int key = min(ch * CHUNK + lane, a.top_k - 1);
-    return __builtin_nontemporal_load(sel_row + key);
+  // Streaming: the selected indices of chunk ch land in sel_ring slot
+  // ch mod kSlots (lanes < CHUNK, each a 4-byte global->LDS load; every wave
+  // issues the same load so that all waves count the same loads).
+  auto load_sel = [&](int ch) {
+    if (lane < CHUNK) {
+      const int key = min(ch * CHUNK + lane, a.top_k - 1);
+      lds_char* const dst = sel_lds + (ch % C::kSlots) * (4 * CHUNK);
+      __builtin_amdgcn_global_load_lds((gbl_char*)(sel_row + key), dst, 4, 0, 0);
+    }
   };
-  // Row pointer of key k0 + lane, and whether this group's query uses it.
-  auto row_of = [&](int ch, int selv, bool& ok) -> const char* {
-    const int key = ch * CHUNK + lane;
-    ok = false;
+  // Streaming: row of key `key` of the query's list given its selected index
+  // (used when key < nsel), and whether the query uses it.
+  auto row_ptr = [&](int key, int selv, bool& ok) -> const char* {
     const char* p = self_row;
-    if constexpr (GROUP == 1) {
-      if (key < nsel) {
-        ok = (selv >= 0) && (selv < nv);
-        if (ok) p = comp_base + (int64_t)selv * kRowBytes;
-      } else if (key < nk) {
-        ok = true;
-        p = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
-      }
-    } else {
-      if (key < n_ab) {
-        const int idx = lds_read_i32(list_lds + 4u * key);
-        lds_wait();
-        const bool in_range = idx >= 0 && idx < a.n_comp;
-        if (in_range) p = comp_base + (int64_t)idx * kRowBytes;
-        if (key < n_a) {  // t0's own selection
-          const bool ok0 = idx >= 0 && idx < nv;  // grp 0: nv is t0's
-          if (grp == 0) {
-            ok = ok0;
-          } else if (in_range && has1) {
-            const unsigned word = (unsigned)lds_read_i32(bm1_lds + 4u * (idx >> 5));
-            lds_wait();
-            ok = (word >> (idx & 31)) & 1u;
-          }
-        } else {  // rows only t1 selected
-          ok = grp == 1;
-        }
-      } else if (key < nk) {
-        const int srow = ws0 + (key - n_ab);
-        p = raw_base + (int64_t)srow * kRowBytes;
-        ok = srow >= ws && srow <= t && q_valid;
-      }
+    ok = false;
+    if (key < nsel) {
+      ok = (selv >= 0) && (selv < nv);
+      if (ok) p = comp_base + (int64_t)selv * kRowBytes;
+    } else if (key < nk) {
+      ok = true;
+      p = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
     }
     return p;
   };
-  // This wave's share of the gather of one chunk, plus (rope in registers)
-  // the rope fragments of the rows this wave scores.
+  // Pair variant: row pointer of key ch*CHUNK + lane of the pair's list, and
+  // whether this group's query uses it.
+  auto row_of_pair = [&](int ch, bool& ok) -> const char* {
+    const int key = ch * CHUNK + lane;
+    ok = false;
+    const char* p = self_row;
+    if (key < n_ab) {
+      int idx = lds_read_i32(list_lds + 4u * key);
+      lds_wait();
+      fence_reg(idx);
+      const bool in_range = idx >= 0 && idx < a.n_comp;
+      if (in_range) p = comp_base + (int64_t)idx * kRowBytes;
+      if (key < n_a) {  // t0's own selection
+        const bool ok0 = idx >= 0 && idx < nv;  // grp 0: nv is t0's
+        if (grp == 0) {
+          ok = ok0;
+        } else if (in_range && has1) {
+          int word = lds_read_i32(bm1_lds + 4u * (idx >> 5));
+          lds_wait();
+          fence_reg(word);
+          ok = ((unsigned)word >> (idx & 31)) & 1u;
+        }
+      } else {  // rows only t1 selected
+        ok = grp == 1;
+      }
+    } else if (key < nk) {
+      const int srow = ws0 + (key - n_ab);
+      p = raw_base + (int64_t)srow * kRowBytes;
+      ok = srow >= ws && srow <= t && q_valid;
+    }
+    return p;
+  };
+  // This wave's share of the gather of one chunk: kRowsPerHw value loads
+  // (one row each, row n's pointer in lane n of kp) and one rope load
+  // covering the same rows (lane l loads part of row row0 + l/8, whose
+  // pointer it holds in kr).
   const int row0 = hw * kRowsPerHw;
-  auto gather = [&](const char* kp, lds_char* buf, half8 (&rope)[2]) {
-    lds_char* bufA = buf;
+  const int rope_row = row0 + min(lane >> 3, kRowsPerHw - 1);
+  auto gather = [&](const char* kp, const char* kr, lds_char* buf) {
     const uintptr_t kpi = (uintptr_t)kp;
     const unsigned kp_lo = (unsigned)kpi;
     const unsigned kp_hi = (unsigned)(kpi >> 32);
@@ -354,45 +439,63 @@ void attn_kernel(AttnArgs a) {
       const unsigned lo = __builtin_amdgcn_readlane(kp_lo, n);
       const unsigned hi = __builtin_amdgcn_readlane(kp_hi, n);
       const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
-      const int off = (lane ^ swz_a(n)) << 4;
-      __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), bufA + n * 1024, 16, 0, 0);
+      const unsigned off = (unsigned)(lane ^ swz_a(n)) << 4;  // zero-extended: SGPR base + VGPR offset form
+      __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), buf + n * 1024, 16, 0, 0);
     }
-    if constexpr (!ROPE_REG) {
-      lds_char* bufB = bufA + C::kBufA;
-      // Rope load j covers rows 8j .. 8j+7; they are dealt to the waves.
-#pragma unroll
-      for (int jj = 0; jj < kRopeLoadsPerHw; ++jj) {
-        const int j = hw + jj * kHw;
-        if (j < CHUNK / 8) {
-          const int nb = 8 * j + (lane >> 3);
-          const unsigned lo = __shfl(kp_lo, nb);
-          const unsigned hi = __shfl(kp_hi, nb);
-          const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
-          const int off = (64 + ((lane & 7) ^ swz_b(nb))) << 4;
-          __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), bufB + 8 * j * 128, 16, 0, 0);
-        }
-      }
-    } else {
-      if (has_rope) {
-        const int nr = 16 * tile + c16;
-        const unsigned lo = __shfl(kp_lo, nr);
-        const unsigned hi = __shfl(kp_hi, nr);
-        const char* rowp = reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
-        rope[0] = *reinterpret_cast<const half8*>(rowp + 1024 + 16 * g);
-        rope[1] = *reinterpret_cast<const half8*>(rowp + 1024 + 64 + 16 * g);
-      }
+    lds_char* const rope_dst = buf + C::kBufA + row0 * 128;
+    if (lane < 8 * kRowsPerHw) {
+      const int off = (64 + ((lane & 7) ^ swz_b(rope_row))) << 4;
+      __builtin_amdgcn_global_load_lds((gbl_char*)(kr + off), rope_dst, 16, 0, 0);
     }
   };
 
-  // Scores, softmax update and PV of one chunk already in `cur`.
-  // With two buffers the S^T exchange area alternates with the chunk buffer,
-  // and no barrier is needed at the end of a chunk: the buffer is refilled
-  // only after the next chunk's barrier, which every wave reaches after its
-  // last read of it.
-  auto compute = [&](lds_char* cur, unsigned long long valid, const half8 (&rope)[2], int sb) {
+  // One chunk in `cur`. All LDS reads of the chunk (this wave's K and V^T
+  // fragments, and for streaming its validity mask) are issued together and
+  // waited for once; after the S^T exchange barrier `cur` is no longer read,
+  // and after_exchange() may start refilling it. No barrier is needed at the
+  // end of a chunk: the S^T area is written again only after a later chunk's
+  // barrier, which every wave reaches after its last read of it.
+  auto compute = [&](lds_char* cur, unsigned long long valid_in, unsigned valid_lds, int sb, auto&& after_exchange) {
     const unsigned bA = (unsigned)(uintptr_t)cur;  // LDS byte address
     float* sbuf_c = sbuf_g + sb * (C::kSBytes / 4);
     const unsigned sbuf_c_addr = sbuf_addr + sb * C::kSBytes;
+
+    // V^T fragments: O^T[dims (512/W) wave + 16nt + 4g + i][head c16] needs,
+    // per PV step, keys kPvKeys*kb + kKpl*g + 4u + tri of dims dv0 + 4*trc ..
+    const int tri = (lane >> 2) & 3;
+    const int trc = lane & 3;
+    // Streaming reads them before the S^T exchange (its buffer is refilled
+    // right after it); the pair variant, which refills only after the next
+    // chunk's barrier, reads them after the exchange (fewer live registers).
+    constexpr bool kEarlyV = GROUP == 1;
+    short4v vt[C::kNt][C::kPvSteps][kUnits];
+    auto read_v = [&]() {
+#pragma unroll
+      for (int nt = 0; nt < C::kNt; ++nt) {
+        const int dv0 = (kDv / WAVES) * wave + 16 * nt;
+        const int unit = (dv0 >> 3) + (trc >> 1);
+        const int sub = (trc & 1) << 3;
+#pragma unroll
+        for (int kb = 0; kb < C::kPvSteps; ++kb)
+#pragma unroll
+          for (int u = 0; u < kUnits; ++u) {
+            const int n = C::kPvKeys * kb + kKpl * g + 4 * u + tri;
+            vt[nt][kb][u] = lds_read_tr16(bA + n * 1024 + ((unit ^ swz_a(n)) << 4) + sub);
+          }
+      }
+    };
+    auto fence_v = [&]() {
+#pragma unroll
+      for (int nt = 0; nt < C::kNt; ++nt)
+#pragma unroll
+        for (int kb = 0; kb < C::kPvSteps; ++kb)
+#pragma unroll
+          for (int u = 0; u < kUnits; ++u) fence_reg(vt[nt][kb][u]);
+    };
+    if constexpr (kEarlyV) read_v();
+    unsigned long long valid = valid_in;
+    if constexpr (GROUP == 1) valid = lds_read_u64(valid_lds);
+
     // The contraction slice is a compile-time constant inside qk(), so each
     // K read address is fixed at compile time (no per-read branches).
     auto qk = [&](auto half_c) {
@@ -400,92 +503,104 @@ void attn_kernel(AttnArgs a) {
       const int n = 16 * tile + c16;
       constexpr int kLen = C::len(HALF);
       constexpr int kStart = C::start(HALF);
-      half8 kf[C::kSteps];
+      // K fragments in two batches (fewer live registers); the first wait
+      // also covers the V^T and mask reads issued before.
+      constexpr int kBatch = (kLen + 1) / 2;
+      auto read_k = [&](half8(&kf)[kBatch], int s0, int cnt) {
 #pragma unroll
-      for (int s = 0; s < kLen; ++s) {
-        const int ks = kStart + s;  // k-step of 32 latent dims
-        if (ks < 16) {
-          kf[s] = lds_read_b128(bA + n * 1024 + (((4 * ks + g) ^ swz_a(n)) << 4));
-        } else if constexpr (!ROPE_REG) {
-          kf[s] = lds_read_b128(bA + C::kBufA + n * 128 + (((4 * (ks - 16) + g) ^ swz_b(n)) << 4));
-        }
-      }
-      lds_wait();
-#pragma unroll
-      for (int s = 0; s < kLen; ++s) {
-        const int ks = kStart + s;
-        if (ROPE_REG && ks >= 16) kf[s] = rope[ks - 16];
-        fence_reg(kf[s]);
-      }
-      // Three independent accumulation chains, summed in a fixed order.
-      float4v sacc[3] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int s = 0; s < kLen; ++s)
-        sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], sacc[s % 3], 0, 0, 0);
-      const float4v ssum = (sacc[0] + sacc[1]) + sacc[2];
-      const int slot = (4 * tile + g) ^ swz_s(c16);
-      *reinterpret_cast<float4v*>(&sbuf_c[(HALF * kHeads + c16) * C::kSStride + 4 * slot]) = ssum;
-    };
-    if (half == 0) {
-      qk(std::integral_constant<int, 0>{});
-    } else if constexpr (C::kHalves == 2) {
-      qk(std::integral_constant<int, 1>{});
-    } else if constexpr (C::kHalves == 4) {
-      if (half == 1) qk(std::integral_constant<int, 1>{});
-      else if (half == 2) qk(std::integral_constant<int, 2>{});
-      else qk(std::integral_constant<int, 3>{});
-    }
-    static_assert(C::kHalves == 1 || C::kHalves == 2 || C::kHalves == 4, "slice dispatch");
-    lds_barrier();
-
-    // Online softmax for head c16 over keys {32kb + 8g + i}.
-    float zz[C::kPvSteps][8];
-    {
-      float4v sp[C::kPvSteps][C::kHalves][2];
-#pragma unroll
-      for (int kb = 0; kb < C::kPvSteps; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < C::kHalves; ++hh) {
-          const unsigned srow = sbuf_c_addr + 4u * ((hh * kHeads + c16) * C::kSStride);
-          const int s0 = (8 * kb + 2 * g) ^ swz_s(c16);
-          const int s1 = (8 * kb + 2 * g + 1) ^ swz_s(c16);
-          sp[kb][hh][0] = lds_read_f4(srow + 16u * s0);
-          sp[kb][hh][1] = lds_read_f4(srow + 16u * s1);
-        }
-      lds_wait();
-#pragma unroll
-      for (int kb = 0; kb < C::kPvSteps; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < C::kHalves; ++hh) {
-          fence_reg(sp[kb][hh][0]);
-          fence_reg(sp[kb][hh][1]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            zz[kb][i] = hh == 0 ? sp[kb][hh][0][i] : zz[kb][i] + sp[kb][hh][0][i];
-            zz[kb][4 + i] = hh == 0 ? sp[kb][hh][1][i] : zz[kb][4 + i] + sp[kb][hh][1][i];
+        for (int s = 0; s < kBatch; ++s) {
+          const int ks = kStart + s0 + s;  // k-step of 32 latent dims
+          if (s < cnt) {
+            if (ks < 16) {
+              kf[s] = lds_read_b128(bA + n * 1024 + (((4 * ks + g) ^ swz_a(n)) << 4));
+            } else {
+              kf[s] = lds_read_b128(bA + C::kBufA + n * 128 + (((4 * (ks - 16) + g) ^ swz_b(n)) << 4));
+            }
           }
         }
-    }
+      };
+      // Three independent accumulation chains, summed in a fixed order.
+      float4v sacc[3] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+      {
+        half8 kf[kBatch];
+        read_k(kf, 0, kBatch);
+        lds_wait();
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) fence_reg(kf[s]);
+        if constexpr (kEarlyV) fence_v();
+        fence_reg(valid);
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s)
+          sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], sacc[s % 3], 0, 0, 0);
+      }
+      if constexpr (kLen > kBatch) {
+        half8 kf[kBatch];
+        read_k(kf, kBatch, kLen - kBatch);
+        lds_wait();
+#pragma unroll
+        for (int s = 0; s < kLen - kBatch; ++s) fence_reg(kf[s]);
+#pragma unroll
+        for (int s = kBatch; s < kLen; ++s)
+          sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s - kBatch], qf[s], sacc[s % 3], 0, 0, 0);
+      }
+      const float4v ssum = (sacc[0] + sacc[1]) + sacc[2];
+      const int slot = s_slot<CHUNK>(4 * tile + g, c16);
+      *reinterpret_cast<float4v*>(&sbuf_c[(HALF * kHeads + c16) * C::kSStride + 4 * slot]) = ssum;
+    };
+    with_slice<C::kHalves>(half, qk);
+    lds_barrier();
+
+    // Online softmax for head c16 over keys kPvKeys*kb + kKpl*g + i. The S^T
+    // reads are issued before after_exchange(), whose own LDS wait covers them.
+    float4v sp[C::kPvSteps][C::kHalves][kUnits];
+#pragma unroll
+    for (int kb = 0; kb < C::kPvSteps; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < C::kHalves; ++hh) {
+        const unsigned srow = sbuf_c_addr + 4u * ((hh * kHeads + c16) * C::kSStride);
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+          const int su = s_slot<CHUNK>((C::kPvKeys / 4) * kb + kUnits * g + u, c16);
+          sp[kb][hh][u] = lds_read_f4(srow + 16u * su);
+        }
+      }
+    if constexpr (!kEarlyV) read_v();
+    after_exchange();
+    lds_wait();
+    if constexpr (!kEarlyV) fence_v();
+    float zz[C::kPvSteps][kKpl];
+#pragma unroll
+    for (int kb = 0; kb < C::kPvSteps; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < C::kHalves; ++hh)
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+          fence_reg(sp[kb][hh][u]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            zz[kb][4 * u + i] = hh == 0 ? sp[kb][hh][u][i] : zz[kb][4 * u + i] + sp[kb][hh][u][i];
+        }
     // Keys past the end of the list (or rejected indices) only occur in
     // chunks that are not entirely valid.
+    const unsigned vlo = __builtin_amdgcn_readfirstlane((unsigned)valid);
+    const unsigned vhi = __builtin_amdgcn_readfirstlane((unsigned)(valid >> 32));
+    const unsigned long long vmask = ((unsigned long long)vhi << 32) | vlo;
     constexpr unsigned long long kChunkMask = CHUNK == 64 ? ~0ull : ((1ull << CHUNK) - 1);
-    if ((valid & kChunkMask) != kChunkMask) {
+    if ((vmask & kChunkMask) != kChunkMask) {
 #pragma unroll
       for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kk = 32 * kb + 8 * g + i;
-          if (!((valid >> kk) & 1ull)) zz[kb][i] = -__builtin_inff();
+        for (int i = 0; i < kKpl; ++i) {
+          const int kk = C::kPvKeys * kb + kKpl * g + i;
+          if (!((vmask >> kk) & 1ull)) zz[kb][i] = -__builtin_inff();
         }
     }
     float cmax = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) cmax = fmaxf(cmax, zz[kb][i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    cmax *= a.scale_log2e;  // scale > 0, so the max commutes with it
+      for (int i = 0; i < kKpl; ++i) cmax = fmaxf(cmax, zz[kb][i]);
+    cmax = max4_heads(cmax) * a.scale_log2e;  // scale > 0, so the max commutes with it
     // Move the reference (and rescale O and l) only when needed; the test is
     // made per head and the branch is taken if any head needs it.
     const bool move = cmax > m_ref + kRescaleThreshold;
@@ -497,52 +612,34 @@ void attn_kernel(AttnArgs a) {
       for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] *= alpha;
     }
     const float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
-    half8 pf[C::kPvSteps];
+    using pvec = std::conditional_t<kKpl == 8, half8, half4>;
+    pvec pf[C::kPvSteps];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kKpl; ++i) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zz[kb][i], a.scale_log2e, -m_use));
         psum += p;
         pf[kb][i] = (_Float16)p;
       }
     l_run += psum;
 
-    // O^T[dims (512/W) wave + 16nt + 4g + i][head c16] += V^T . P^T
-    const int tri = (lane >> 2) & 3;
-    const int trc = lane & 3;
-    constexpr int kPvGroup = C::kNt * C::kPvSteps > 4 ? (4 / C::kPvSteps > 0 ? 4 / C::kPvSteps : 1) : C::kNt;
+    // O^T += V^T . P^T
 #pragma unroll
-    for (int nt0 = 0; nt0 < C::kNt; nt0 += kPvGroup) {
-      short4v vt[kPvGroup][C::kPvSteps][2];
+    for (int nt = 0; nt < C::kNt; ++nt)
 #pragma unroll
-      for (int j = 0; j < kPvGroup; ++j) {
-        const int dv0 = (kDv / WAVES) * wave + 16 * (nt0 + j);
-        const int unit = (dv0 >> 3) + (trc >> 1);
-        const int sub = (trc & 1) << 3;
-#pragma unroll
-        for (int kb = 0; kb < C::kPvSteps; ++kb) {
-          const int n_lo = 32 * kb + 8 * g + tri;
-          const int n_hi = n_lo + 4;
-          vt[j][kb][0] = lds_read_tr16(bA + n_lo * 1024 + ((unit ^ swz_a(n_lo)) << 4) + sub);
-          vt[j][kb][1] = lds_read_tr16(bA + n_hi * 1024 + ((unit ^ swz_a(n_hi)) << 4) + sub);
+      for (int kb = 0; kb < C::kPvSteps; ++kb) {
+        if constexpr (kKpl == 8) {
+          const half4 hlo = __builtin_bit_cast(half4, vt[nt][kb][0]);
+          const half4 hhi = __builtin_bit_cast(half4, vt[nt][kb][1]);
+          const half8 vf = half8{hlo[0], hlo[1], hlo[2], hlo[3], hhi[0], hhi[1], hhi[2], hhi[3]};
+          acc_o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[kb], acc_o[nt], 0, 0, 0);
+        } else {
+          const half4 vf = __builtin_bit_cast(half4, vt[nt][kb][0]);
+          acc_o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf[kb], acc_o[nt], 0, 0, 0);
         }
       }
-      lds_wait();
-#pragma unroll
-      for (int j = 0; j < kPvGroup; ++j)
-#pragma unroll
-        for (int kb = 0; kb < C::kPvSteps; ++kb) {
-          fence_reg(vt[j][kb][0]);
-          fence_reg(vt[j][kb][1]);
-          const half4 hlo = __builtin_bit_cast(half4, vt[j][kb][0]);
-          const half4 hhi = __builtin_bit_cast(half4, vt[j][kb][1]);
-          const half8 vf = half8{hlo[0], hlo[1], hlo[2], hlo[3], hhi[0], hhi[1], hhi[2], hhi[3]};
-          acc_o[nt0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[kb], acc_o[nt0 + j], 0, 0, 0);
-        }
-    }
-    if constexpr (NBUF == 1) lds_barrier();  // `cur` and sbuf are refilled next
   };
 
   if (c_begin >= c_end) {  // an empty split: a neutral partial
@@ -556,45 +653,89 @@ void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // Prologue: start the gather of the first chunk, then load Q^T while it
-  // flies.
-  unsigned long long valid_cur;
-  half8 rope_cur[2], rope_nxt[2];
-  {
-    const int sel0 = load_sel(c_begin);
-    bool ok0;
-    const char* kp0 = row_of(c_begin, sel0, ok0);
-    valid_cur = __ballot(ok0);
-    gather(kp0, buf0, rope_cur);
-  }
-  {
+  // Q^T fragments of this wave's contraction slice (registers, whole query).
+  auto load_q = [&]() {
     const _Float16* qrow = a.q + ((int64_t)(q_valid ? r : r - 1) * kHeads + c16) * kDqk + 8 * g;
     const int q_start = C::start(half), q_len = C::len(half);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
       if (s < q_len) qf[s] = *reinterpret_cast<const half8*>(qrow + 32 * (q_start + s));
-  }
-  int sel_next = load_sel(min(c_begin + 1, c_end - 1));
+  };
 
-  if constexpr (NBUF == 2) {
-    // Chunk ch computes from `cur` while the gather of chunk ch+1 lands in
-    // `nxt`. The only wait is for this chunk's gather (and everything issued
-    // before it), right before the barrier that publishes it.
+  if constexpr (GROUP == 1) {
+    auto buf_of = [&](int ch) { return bufs + (ch % NBUF) * C::kBuf; };
+    // Gather of chunk ch into its ring buffer and its validity mask into its
+    // slot; its selected indices are already in LDS.
+    auto issue = [&](int ch) {
+      const int slot = ch % C::kSlots;
+      int s_main = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + min(lane, CHUNK - 1)));
+      int s_rope = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + rope_row));
+      lds_wait();
+      fence_reg(s_main);
+      fence_reg(s_rope);
+      bool ok, ok_rope;
+      const char* kp = row_ptr(ch * CHUNK + lane, s_main, ok);
+      const char* kr = row_ptr(ch * CHUNK + rope_row, s_rope, ok_rope);
+      const unsigned long long vm = __ballot(ok && lane < CHUNK);
+      if (hw == 0 && lane == 0) valid_slots[slot] = vm;
+      gather(kp, kr, buf_of(ch));
+    };
+    // Prologue: Q fragments and the indices of the first NBUF+1 chunks, all
+    // waited for; then the gathers of the first NBUF chunks, each followed by
+    // the index load for the chunk NBUF+1 places later (the order of loads
+    // of the loop, where iteration ch issues chunk ch+NBUF and the indices of
+    // chunk ch+2*NBUF+1).
+    load_q();
+#pragma unroll
+    for (int k = 0; k <= NBUF; ++k) load_sel(c_begin + k);
+    wait_vmcnt<0>();
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) {
+      if (c_begin + k < c_end) {
+        issue(c_begin + k);
+        load_sel(c_begin + k + NBUF + 1);
+      }
+    }
+    for (int ch = c_begin; ch < c_end; ++ch) {
+      // Chunk ch's loads (and all before them) are complete once at most
+      // kWaitAhead later ones are outstanding, provided the chunks up to
+      // ch+NBUF-1 were all issued; near the end, wait for everything.
+      if (ch + NBUF - 1 < c_end) wait_vmcnt<C::kWaitAhead>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      compute(buf_of(ch), 0ull, valid_addr + 8u * (ch % C::kSlots), 0, [&]() {
+        if (ch + NBUF < c_end) {
+          issue(ch + NBUF);
+          load_sel(ch + 2 * NBUF + 1);
+        }
+      });
+    }
+    wait_vmcnt<0>();  // index loads for chunks past the end
+  } else {
+    // Pair variant: two buffers, chunk ch computes from `cur` while the
+    // gather of chunk ch+1 lands in `nxt`.
+    lds_char* const buf0 = bufs;
+    lds_char* const buf1 = bufs + C::kBuf;
+    auto gather_pair = [&](int ch, lds_char* buf) -> unsigned long long {
+      bool ok;
+      const char* kp = row_of_pair(ch, ok);
+      const uintptr_t kpi = (uintptr_t)kp;
+      const unsigned lo = __shfl((unsigned)kpi, rope_row);
+      const unsigned hi = __shfl((unsigned)(kpi >> 32), rope_row);
+      const unsigned long long vm = __ballot(ok);
+      gather(kp, reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo), buf);
+      return vm;
+    };
+    unsigned long long valid_cur = gather_pair(c_begin, buf0);
+    load_q();
     auto step = [&](int ch, lds_char* cur, lds_char* nxt) {
       wait_vmcnt<0>();
       lds_barrier();
       unsigned long long valid_next = 0;
-      if (ch + 1 < c_end) {
-        bool okn;
-        const char* kpn = row_of(ch + 1, sel_next, okn);
-        valid_next = __ballot(okn);
-        sel_next = load_sel(min(ch + 2, c_end - 1));
-        gather(kpn, nxt, rope_nxt);
-      }
-      compute(cur, valid_cur, rope_cur, ch & 1);
+      if (ch + 1 < c_end) valid_next = gather_pair(ch + 1, nxt);
+      compute(cur, valid_cur, 0u, ch & 1, [] {});
       valid_cur = valid_next;
-      rope_cur[0] = rope_nxt[0];
-      rope_cur[1] = rope_nxt[1];
     };
     for (int ch = c_begin;;) {
       step(ch, buf0, buf1);
@@ -602,23 +743,9 @@ void attn_kernel(AttnArgs a) {
       step(ch, buf1, buf0);
       if (++ch >= c_end) break;
     }
-  } else {
-    for (int ch = c_begin; ch < c_end; ++ch) {
-      wait_vmcnt<0>();
-      lds_barrier();
-      compute(buf0, valid_cur, rope_cur, 0);
-      if (ch + 1 < c_end) {
-        bool okn;
-        const char* kpn = row_of(ch + 1, sel_next, okn);
-        valid_cur = __ballot(okn);
-        sel_next = load_sel(min(ch + 2, c_end - 1));
-        gather(kpn, buf0, rope_cur);
-      }
-    }
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot = l_tot + __shfl_xor(l_tot, 32);
+  const float l_tot = sum4_heads(l_run);
   if (a.splits > 1) {
     // Partial result of this split: O and l relative to the reference m
     // (log2 units); attn_merge_kernel combines the splits of a query.
@@ -655,9 +782,6 @@ void attn_kernel(AttnArgs a) {
 #endif
 #ifndef SPMLA_ATTN_WPE
 #define SPMLA_ATTN_WPE 2
-#endif
-#ifndef SPMLA_ATTN_ROPE_REG
-#define SPMLA_ATTN_ROPE_REG 0
 #endif
 
 // Combines the key splits of one (query, head): with M the largest split
@@ -731,8 +855,7 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
   if (a.splits < 1) a.splits = 1;
   const int per_xcd = (a.n_q * a.splits + kXcds - 1) / kXcds;
   constexpr int W = SPMLA_ATTN_WAVES;
-  hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE,
-                                  (bool)SPMLA_ATTN_ROPE_REG, 1>),
+  hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE, 1>),
                      dim3(per_xcd * kXcds), dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
@@ -749,8 +872,7 @@ hipError_t launch_attn_grouped(const AttnArgs& a_in, hipStream_t stream) {
   // Bitmaps of the two queries' rows and the pair's row list.
   const size_t words = ((size_t)a.n_comp + 31) / 32;
   const size_t lds = 4 * (2 * words + 2 * (size_t)a.top_k);
-  hipLaunchKernelGGL((attn_kernel<SPMLA_ATTN_WAVES, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE,
-                                  (bool)SPMLA_ATTN_ROPE_REG, 2>),
+  hipLaunchKernelGGL((attn_kernel<SPMLA_ATTN_WAVES, SPMLA_ATTN_CHUNK, 2, SPMLA_ATTN_WPE, 2>),
                      dim3(per_xcd * kXcds), dim3(128 * SPMLA_ATTN_WAVES), lds, stream, a);
   return hipGetLastError();
 }
