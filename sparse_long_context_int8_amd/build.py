@@ -19,6 +19,10 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libspmla.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attn.hip", "compress.hip"]
 ARCH = "gfx950"
+# Per-source code generation options. The int8 indexer kernels consume every
+# matrix-core result with vector ops at once; the VGPR form of the MFMA
+# instructions saves an accumulator-register read per result element.
+EXTRA_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -45,7 +49,7 @@ def common_flags() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -24,6 +24,19 @@ namespace spmla {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+// The weights of one token as two int16 pairs (heads 0,1 and 2,3) for the
+// packed head sum below.
+struct HeadWeights {
+  v2s w01, w23;
+};
+__device__ __forceinline__ HeadWeights head_weights(int wpack) {
+  HeadWeights w;
+  w.w01 = v2s{(short)(int8_t)(wpack & 0xff), (short)(int8_t)((wpack >> 8) & 0xff)};
+  w.w23 = v2s{(short)(int8_t)((wpack >> 16) & 0xff), (short)(int8_t)((wpack >> 24) & 0xff)};
+  return w;
+}
 
 constexpr int kQTile = 64;  // query tokens per workgroup (16 per wave)
 constexpr int kJStep = 64;  // compressed rows per step (4 MFMA column tiles)
@@ -33,7 +46,7 @@ constexpr int kJStep = 64;  // compressed rows per step (4 MFMA column tiles)
 // receives in each tile, with its weights and visible-row count.
 struct TokenTiles {
   v4i afrag[4];
-  int wpack[4];  // 4 x int8 weights of the lane's token in tile m
+  HeadWeights w[4];  // weights of the lane's token in tile m
   int tok[4];
   int nv[4];
 
@@ -47,7 +60,7 @@ struct TokenTiles {
       afrag[m] = tok_a < n_q ? *reinterpret_cast<const v4i*>(iq + (int64_t)row * kIdxDim + grp * 16)
                              : v4i{0, 0, 0, 0};
       tok[m] = t_base + 4 * m + grp;
-      wpack[m] = tok[m] < n_q ? *reinterpret_cast<const int*>(iw + (int64_t)tok[m] * kIdxHeads) : 0;
+      w[m] = head_weights(tok[m] < n_q ? *reinterpret_cast<const int*>(iw + (int64_t)tok[m] * kIdxHeads) : 0);
       nv[m] = min(n_comp, (q_pos0 + tok[m] + 1) / ratio);
     }
   }
@@ -63,14 +76,15 @@ __device__ __forceinline__ void load_b(const int8_t* ik, int n_comp, int j0, int
 }
 
 // Weighted head sum of one 16x16 result: the 4 heads of the lane's token.
-__device__ __forceinline__ int head_sum(v4i acc, int wpack) {
-  int v = 0;
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int wh = (int)(int8_t)((wpack >> (8 * h)) & 0xff);
-    v += wh * max(acc[h], 0);
-  }
-  return v;
+// Each head dot product is at most 64 * 64 = 4096 in magnitude, so it packs
+// exactly into int16; ReLU and the weighted sum then run as two packed
+// maxima and two int16 dot products with int32 accumulation (exact).
+__device__ __forceinline__ int head_sum(v4i acc, const HeadWeights& w) {
+  v2s p01 = __builtin_bit_cast(v2s, __builtin_amdgcn_perm((unsigned)acc[1], (unsigned)acc[0], 0x05040100u));
+  v2s p23 = __builtin_bit_cast(v2s, __builtin_amdgcn_perm((unsigned)acc[3], (unsigned)acc[2], 0x05040100u));
+  p01 = __builtin_elementwise_max(p01, v2s{0, 0});
+  p23 = __builtin_elementwise_max(p23, v2s{0, 0});
+  return __builtin_amdgcn_sdot2(p23, w.w23, __builtin_amdgcn_sdot2(p01, w.w01, 0, false), false);
 }
 
 // Scores of the lane's token in tile m for rows j0+4c .. j0+4c+3.
@@ -79,7 +93,7 @@ __device__ __forceinline__ v4i tile_scores(const TokenTiles& tt, int m, const v4
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt.afrag[m], b[u], v4i{0, 0, 0, 0}, 0, 0, 0);
-    s[u] = head_sum(acc, tt.wpack[m]);
+    s[u] = head_sum(acc, tt.w[m]);
   }
   return s;
 }
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
                         ? *reinterpret_cast<const v4i*>(a.iq + ((int64_t)4 * t0 + col) * kIdxDim + grp * 16)
                         : v4i{0, 0, 0, 0};
   const int tok = t0 + grp;
-  const int wpack = tok < a.n_q ? *reinterpret_cast<const int*>(a.iw + (int64_t)tok * kIdxHeads) : 0;
+  const HeadWeights hw = head_weights(tok < a.n_q ? *reinterpret_cast<const int*>(a.iw + (int64_t)tok * kIdxHeads) : 0);
   const int nv = tok < a.n_q ? min(a.n_comp, (a.q_pos0 + tok + 1) / a.ratio) : 0;
   const int t_last = min(t0 + 3, a.n_q - 1);
   const int nv_max = min(a.n_comp, (a.q_pos0 + t_last + 1) / a.ratio);
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
     for (int q = 0; q < kUnroll; ++q) {
       const int j = stride * (16 * (s0 + q) + col);
       const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, b[q], v4i{0, 0, 0, 0}, 0, 0, 0);
-      if (s0 + q < n_steps && j < nv) atomicAdd(&hist[grp][score_code(head_sum(acc, wpack))], 1);
+      if (s0 + q < n_steps && j < nv) atomicAdd(&hist[grp][score_code(head_sum(acc, hw))], 1);
     }
   }
   __syncthreads();
@@ -258,10 +272,12 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
 
 // Collect pass: the indexer's 64-token x span tiling with exact scores; every
 // visible score >= the token's threshold is written as (score, row) into the
-// token's slots for this span, in row order. The 16 lanes holding one token
-// in a tile assign slots with a prefix sum; the slot count written at the end
-// is the true count, so the finish pass can detect a full span.
+// token's slots for this span. Slots are claimed with an LDS counter per
+// token (only the token's own wave touches it), so the order inside a span is
+// arrival order; the finish pass orders candidates exactly. The count written
+// at the end is the true count, so the finish pass can detect a full span.
 __global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
+  __shared__ int claimed[kQTile];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t_base = blockIdx.y * kQTile + wave * 16;
@@ -273,16 +289,18 @@ __global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
   const int nv_wave = min(a.n_comp, (a.q_pos0 + t_last + 1) / a.ratio);
   const int col = lane & 15, grp = lane >> 4;
   const int cap = a.plan.cap;
+  int* const cnt = claimed + wave * 16;  // this wave's 16 tokens, local index 4m + grp
+  if (lane < 16) cnt[lane] = 0;
 
   TokenTiles tt;
   tt.load(a.iq, a.iw, a.n_q, a.q_pos0, a.n_comp, a.ratio, t_base, col, grp);
-  int thr[4], run[4];
+  int thr[4], lim[4];
   int32_t* slots[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const bool ok = tt.tok[m] < a.n_q;
     thr[m] = ok ? a.thresh[tt.tok[m]] : INT32_MAX;
-    run[m] = 0;
+    lim[m] = ok ? min(tt.nv[m], j_end) : 0;  // rows below lim are visible and in the span
     slots[m] = a.cand + 2 * (((int64_t)(ok ? tt.tok[m] : 0) * a.plan.n_spans + span_idx) * cap);
   }
 
@@ -291,38 +309,35 @@ __global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
     v4i bfrag[4];
     load_b(a.ik, a.n_comp, j0, col, grp, bfrag);
     const int jl = j0 + 4 * col;
+    v4i sc[4];
+    int c[4], base[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const v4i s = tile_scores(tt, m, bfrag);
-      bool pass[4];
-      int c = 0;
+      sc[m] = tile_scores(tt, m, bfrag);
+      c[m] = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[m] += (jl + u < lim[m] && sc[m][u] >= thr[m]) ? 1 : 0;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) base[m] = c[m] ? atomicAdd(&cnt[4 * m + grp], c[m]) : 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (c[m] == 0) continue;
+      int pos = base[m];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        pass[u] = tt.tok[m] < a.n_q && jl + u < tt.nv[m] && jl + u < j_end && s[u] >= thr[m];
-        c += pass[u] ? 1 : 0;
-      }
-      // Inclusive prefix over the 16 lanes of this token.
-      int incl = c;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const int y = __shfl_up(incl, o, 16);
-        if (col >= o) incl += y;
-      }
-      const int tot = __shfl(incl, 15, 16);
-      int pos = run[m] + incl - c;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pass[u]) {
-          if (pos < cap) *reinterpret_cast<int2*>(slots[m] + 2 * pos) = int2{s[u], jl + u};
+        if (jl + u < lim[m] && sc[m][u] >= thr[m]) {
+          if (pos < cap) *reinterpret_cast<int2*>(slots[m] + 2 * pos) = int2{sc[m][u], jl + u};
           ++pos;
         }
       }
-      run[m] += tot;
     }
   }
+  if (col == 0) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    if (col == 0 && tt.tok[m] < a.n_q) a.counts[(int64_t)tt.tok[m] * a.plan.n_spans + span_idx] = run[m];
+    for (int m = 0; m < 4; ++m)
+      if (tt.tok[m] < a.n_q) a.counts[(int64_t)tt.tok[m] * a.plan.n_spans + span_idx] = cnt[4 * m + grp];
+  }
 }
 
 }  // namespace

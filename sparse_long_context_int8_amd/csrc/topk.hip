@@ -92,11 +92,11 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, i
   __syncthreads();
 }
 
-// Bucket offsets, largest bucket first: boff[b] = elements in buckets above
-// b; hist[] (the counts) becomes the fill cursor of each bucket. Ends with a
-// barrier.
+// Bucket offsets, largest bucket first: hist[b] (the count of bucket b)
+// becomes the number of elements in buckets above b, i.e. the fill cursor of
+// bucket b. Ends with a barrier.
 template <int BLOCK>
-__device__ __forceinline__ void bucket_offsets(int* hist, int* boff, int* red) {
+__device__ __forceinline__ void bucket_offsets(int* hist, int* red) {
   constexpr int kPer = kBins1 / BLOCK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tot = 0;
@@ -111,7 +111,6 @@ __device__ __forceinline__ void bucket_offsets(int* hist, int* boff, int* red) {
   for (int i = 0; i < kPer; ++i) {
     const int b = kBins1 - 1 - (tid * kPer + i);
     const int c = hist[b];
-    boff[b] = base;
     hist[b] = base;
     base += c;
   }
@@ -131,7 +130,6 @@ template <int BLOCK, int PER, int SRC>
 __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f, int r) {
   constexpr int NW = BLOCK / 64;
   __shared__ int hist[kBins1];
-  __shared__ int boff[kBins1];
   __shared__ int red_a[NW], red_b[NW], red_c[NW];
   __shared__ int s_bin, s_above, s_count, s_cnt;
   __shared__ int aux[BLOCK + 1];  // span offsets (candidates) or the query row (recompute)
@@ -365,7 +363,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   }
   __syncthreads();
 
-  bucket_offsets<BLOCK>(hist, boff, red_c);
+  bucket_offsets<BLOCK>(hist, red_c);
   const int n_coll = min(s_cnt, cap);
   u64* bucketed = keys + cap;
   for (int e = tid; e < n_coll; e += BLOCK) {
@@ -378,7 +376,9 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   for (int p = tid; p < n_coll; p += BLOCK) {
     const u64 key = bucketed[p];
     const int b = (int)((key - thresh) >> shb);
-    const int st = boff[b], en = hist[b];
+    // After the scatter hist[b] is the end of bucket b, and the end of the
+    // bucket above (placed before it) is its start.
+    const int st = b + 1 < kBins1 ? hist[b + 1] : 0, en = hist[b];
     int place = st;
     for (int q = st; q < en; ++q) place += bucketed[q] > key ? 1 : 0;
     if (place < nsel) sel_row[place] = (nv - 1) - (int)(key & emask);
