@@ -147,8 +147,10 @@ struct Cfg {
   static constexpr int kSBytes = kHalves * kHeads * kSStride * 4;
   static constexpr int kSBufs = GROUP == 1 ? 1 : 2;  // S^T exchange areas per query
   // Streaming (GROUP == 1): selected indices and validity masks of the
-  // chunks in flight, slot = chunk mod kSlots.
-  static constexpr int kSlots = GROUP == 1 ? 2 * NBUF + 2 : 1;
+  // chunks in flight (at most 2 * NBUF + 2), slot = chunk mod kSlots, a power
+  // of two.
+  static constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+  static constexpr int kSlots = GROUP == 1 ? pow2_at_least(2 * NBUF + 2) : 1;
   static constexpr int kLds = NBUF * kBuf + GROUP * kSBufs * kSBytes + kSlots * (4 * CHUNK + 8);
   // Global->LDS loads a wave issues per chunk: its rows, one rope load, and
   // (streaming) the selected indices of a later chunk.
@@ -373,7 +375,7 @@ void attn_kernel(AttnArgs a) {
   auto load_sel = [&](int ch) {
     if (lane < CHUNK) {
       const int key = min(ch * CHUNK + lane, a.top_k - 1);
-      lds_char* const dst = sel_lds + (ch % C::kSlots) * (4 * CHUNK);
+      lds_char* const dst = sel_lds + ((unsigned)ch % C::kSlots) * (4 * CHUNK);
       __builtin_amdgcn_global_load_lds((gbl_char*)(sel_row + key), dst, 4, 0, 0);
     }
   };
@@ -663,11 +665,11 @@ void attn_kernel(AttnArgs a) {
   };
 
   if constexpr (GROUP == 1) {
-    auto buf_of = [&](int ch) { return bufs + (ch % NBUF) * C::kBuf; };
+    auto buf_of = [&](int ch) { return bufs + ((unsigned)ch % NBUF) * C::kBuf; };
     // Gather of chunk ch into its ring buffer and its validity mask into its
     // slot; its selected indices are already in LDS.
     auto issue = [&](int ch) {
-      const int slot = ch % C::kSlots;
+      const int slot = (int)((unsigned)ch % C::kSlots);
       int s_main = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + min(lane, CHUNK - 1)));
       int s_rope = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + rope_row));
       lds_wait();
@@ -704,7 +706,7 @@ void attn_kernel(AttnArgs a) {
       if (ch + NBUF - 1 < c_end) wait_vmcnt<C::kWaitAhead>();
       else wait_vmcnt<0>();
       lds_barrier();
-      compute(buf_of(ch), 0ull, valid_addr + 8u * (ch % C::kSlots), 0, [&]() {
+      compute(buf_of(ch), 0ull, valid_addr + 8u * ((unsigned)ch % C::kSlots), 0, [&]() {
         if (ch + NBUF < c_end) {
           issue(ch + NBUF);
           load_sel(ch + 2 * NBUF + 1);
