@@ -49,6 +49,19 @@ typedef __attribute__((address_space(1))) const char gbl_char;
 constexpr int kRowBytes = kDqk * 2;  // 1152: one latent row
 constexpr int kXcds = 8;             // accelerator complex dies, round-robin dispatch
 
+// Work items are cut into 2 * kXcds contiguous slices of slice_len items; die
+// x takes slice 2*kXcds-1-x, then slice x (blockIdx.x = x + kXcds * l). Each
+// die keeps runs of neighbouring queries (their window rows stay in its L2),
+// and when the cost of a query grows with its position (the first band of a
+// prefill: more visible rows) every die gets one later and one earlier slice,
+// the later one first.
+__host__ __device__ inline int attn_slice_len(int n_items) { return (n_items + 2 * kXcds - 1) / (2 * kXcds); }
+__device__ inline int attn_item(int n_items) {
+  const int slice_len = attn_slice_len(n_items);
+  const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+  return l < slice_len ? (2 * kXcds - 1 - x) * slice_len + l : x * slice_len + (l - slice_len);
+}
+
 // XOR swizzles of the 16-byte units of the LDS images, as linear maps of
 // the row index bits. They were chosen by measuring the LDS bank-conflict
 // counter on gfx950 for every access pattern of this kernel (K-fragment
@@ -247,12 +260,9 @@ void attn_kernel(AttnArgs a) {
   const unsigned sel_ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)sel_ring;
   const unsigned valid_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned long long*)valid_ring;
 
-  // Work items (query r, key split s; or a query pair) are dealt to the dies
-  // in contiguous blocks so that the window rows shared by neighbouring
-  // queries stay in one die's L2.
+  // Work items: (query r, key split s), or a query pair; see attn_item.
   const int n_items = GROUP == 1 ? a.n_q * a.splits : (a.n_q + 1) / 2;
-  const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int item = attn_item(n_items);
   if (item >= n_items) return;
 
   const int lane = threadIdx.x & 63;
@@ -855,10 +865,10 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
   if (a_in.n_q <= 0) return hipSuccess;
   AttnArgs a = a_in;
   if (a.splits < 1) a.splits = 1;
-  const int per_xcd = (a.n_q * a.splits + kXcds - 1) / kXcds;
+  const int grid = 2 * kXcds * attn_slice_len(a.n_q * a.splits);
   constexpr int W = SPMLA_ATTN_WAVES;
   hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE, 1>),
-                     dim3(per_xcd * kXcds), dim3(64 * W), 0, stream, a);
+                     dim3(grid), dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_q * kHeads), dim3(kDv / 4), 0, stream, a);
@@ -870,12 +880,12 @@ hipError_t launch_attn_grouped(const AttnArgs& a_in, hipStream_t stream) {
   AttnArgs a = a_in;
   a.splits = 1;
   const int pairs = (a.n_q + 1) / 2;
-  const int per_xcd = (pairs + kXcds - 1) / kXcds;
+  const int grid = 2 * kXcds * attn_slice_len(pairs);
   // Bitmaps of the two queries' rows and the pair's row list.
   const size_t words = ((size_t)a.n_comp + 31) / 32;
   const size_t lds = 4 * (2 * words + 2 * (size_t)a.top_k);
   hipLaunchKernelGGL((attn_kernel<SPMLA_ATTN_WAVES, SPMLA_ATTN_CHUNK, 2, SPMLA_ATTN_WPE, 2>),
-                     dim3(per_xcd * kXcds), dim3(128 * SPMLA_ATTN_WAVES), lds, stream, a);
+                     dim3(grid), dim3(128 * SPMLA_ATTN_WAVES), lds, stream, a);
   return hipGetLastError();
 }
 
