@@ -822,7 +822,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
     // l sum in split order (a fixed order for every launch)
     float wl = w * l;
     float total = 0.f;
-    for (int s = 0; s < ns; ++s) total += __shfl(wl, s);
+    for (int s = 0; s < ns; ++s) total += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
     if (tid == 0) {
       s_lsum = total;
       s_mmax = m_max;

@@ -36,23 +36,28 @@ constexpr int kBins1 = 2048;  // coarse-pass and ordering bins (11 bits)
 constexpr int kBits1 = 11;
 constexpr int kSlack = 512;  // elements beyond k a workgroup may collect and order
 
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+// Wave-wide scans and reductions with DPP (no LDS round trips): row_shr:n
+// shifts within each 16-lane row (lanes without a source take the identity),
+// then row_bcast:15 / row_bcast:31 (GCN/CDNA only) carry row totals into the
+// rows above. The inclusive result of lane 63 is the wave total.
+template <typename Op>
+__device__ __forceinline__ int wave_incl(int v, int id, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));  // row_bcast:15 -> rows 1, 3
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));  // row_bcast:31 -> rows 2, 3
   return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  return __builtin_amdgcn_readlane(wave_incl(v, INT32_MIN, [](int x, int y) { return max(x, y); }), 63);
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  return __builtin_amdgcn_readlane(wave_incl(v, INT32_MAX, [](int x, int y) { return min(x, y); }), 63);
 }
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
-  return v;
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  return wave_incl(v, 0, [](int x, int y) { return x + y; });
 }
 
 // Bins are scanned from the top. Finds the bin b in which the running count
@@ -353,7 +358,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     if (m == 0) continue;  // wave-uniform
     int base = 0;
     if (lane == 0) base = atomicAdd(&s_cnt, __popcll(m));
-    base = __shfl(base, 0);
+    base = __builtin_amdgcn_readlane(base, 0);  // every lane is active here
     const int pos = base + __popcll(m & below);
     if (take && pos < cap) {  // pos < cap by construction
       const u64 key = key_of(i);
