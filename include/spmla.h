@@ -213,8 +213,10 @@ int spmla_compress(const spmla_desc* desc, const uint16_t* kv_raw, uint16_t* kv_
 
 /*
  * Workspace bytes spmla_prefill needs for this descriptor: one band of
- * indexer scores plus one band of selected rows. Returns SPMLA_OK and
- * writes *bytes, or an error code.
+ * indexer scores (or, when larger, the fused selection's candidate slots or
+ * the key-split partials of a small call) plus two bands of selected rows
+ * (score order, and ascending row order for the attention's gathers).
+ * Returns SPMLA_OK and writes *bytes, or an error code.
  */
 int spmla_prefill_workspace_bytes(const spmla_desc* desc, size_t* bytes);
 
@@ -222,7 +224,10 @@ int spmla_prefill_workspace_bytes(const spmla_desc* desc, size_t* bytes);
  * Steps 1-4 for all n_q queries, band by band: for each band of `band`
  * queries, indexer -> top-k -> attention, all enqueued on `stream` with no
  * host round trip. Same inputs and outputs as the three calls above;
- * sel_out (int32 [n_q][top_k]) and lse may be NULL.
+ * sel_out (int32 [n_q][top_k]) and lse may be NULL. When the compressed
+ * rows exceed 4 MiB the attention takes each selection in ascending row
+ * order, so out and lse can differ from spmla_sparse_attn on sel_out in
+ * fp32 summation order (not beyond the parity tolerance).
  */
 int spmla_prefill(const spmla_desc* desc, const uint16_t* q, const uint16_t* kv_comp,
                   const uint16_t* kv_raw, const int8_t* iq, const int8_t* iw, const int8_t* ik,

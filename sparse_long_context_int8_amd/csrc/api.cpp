@@ -90,6 +90,9 @@ size_t sel_bytes_per_band(const spmla_desc* d) {
   return (size_t)rows * (size_t)d->top_k * sizeof(int32_t);
 }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr size_t kRowBytes = (size_t)spmla::kDqk * 2;  // one fp16 latent row
+constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator die
 // Per-band scratch, reused by the steps of a band in stream order: the score
 // band of the dense selection or the fused selection's thresholds, slot
 // counts and candidates, then the attention's key-split partials (small
@@ -186,6 +189,7 @@ int spmla_topk(const spmla_desc* d, const int32_t* scores, int32_t* sel, int32_t
   a.ld_scores = d->n_comp;
   a.sel = sel;
   a.n_sel = n_sel;
+  a.sel_asc = nullptr;
   a.n_q = d->n_q;
   a.q_pos0 = d->q_pos0;
   a.n_comp = d->n_comp;
@@ -244,7 +248,7 @@ int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (!bytes) return fail(SPMLA_EINVAL, "bytes is NULL");
-  *bytes = band_scratch_bytes(d) + round_up(sel_bytes_per_band(d), 256);
+  *bytes = band_scratch_bytes(d) + 2 * round_up(sel_bytes_per_band(d), 256);
   return ok();
 }
 
@@ -276,6 +280,12 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
   char* ws = static_cast<char*>(workspace);
   int32_t* band_scores = reinterpret_cast<int32_t*>(ws);
   int32_t* band_sel = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d));
+  // Attention takes each selection in ascending row order when the
+  // compressed rows outgrow one die's L2: the queries in flight on a die then
+  // sweep the rows together and share what they gather (the softmax does not
+  // depend on the order of its keys).
+  const bool ascending = (size_t)d->n_comp * kRowBytes > kDieL2Bytes;
+  int32_t* band_sel_asc = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d) + round_up(sel_bytes_per_band(d), 256));
 
   for (int64_t b0 = 0; b0 < d->n_q; b0 += d->band) {
     const int bn = (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band);
@@ -290,6 +300,7 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       fa.ik = ik;
       fa.sel = sel;
       fa.n_sel = nullptr;
+      fa.sel_asc = ascending ? band_sel_asc : nullptr;
       fa.n_q = bn;
       fa.q_pos0 = pos0;
       fa.n_comp = d->n_comp;
@@ -321,6 +332,7 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       ta.ld_scores = band_ld(d);
       ta.sel = sel;
       ta.n_sel = nullptr;
+      ta.sel_asc = ascending ? band_sel_asc : nullptr;
       ta.n_q = bn;
       ta.q_pos0 = pos0;
       ta.n_comp = d->n_comp;
@@ -330,7 +342,7 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       if (rc) return rc;
     }
 
-    spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
+    spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, ascending ? band_sel_asc : sel,
                                    out + b0 * spmla::kHeads * spmla::kDv,
                                    lse ? lse + b0 * spmla::kHeads : nullptr);
     aa.n_q = bn;

@@ -39,6 +39,7 @@ struct TopkArgs {
   int64_t ld_scores;
   int32_t* sel;           // [n_q][top_k]
   int32_t* n_sel;         // [n_q] or null
+  int32_t* sel_asc;       // [n_q][top_k] or null: the same rows in ascending order, -1 padded
   int32_t n_q;
   int32_t q_pos0;
   int32_t n_comp;
@@ -66,6 +67,7 @@ struct FusedArgs {
   const int8_t* ik;  // [n_comp][64]
   int32_t* sel;      // [n_q][top_k]
   int32_t* n_sel;    // [n_q] or null
+  int32_t* sel_asc;  // [n_q][top_k] or null (see TopkArgs)
   int32_t n_q;
   int32_t q_pos0;
   int32_t n_comp;

@@ -150,6 +150,8 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
 
   if (nsel == 0) {
     for (int i = tid; i < k; i += BLOCK) sel_row[i] = -1;
+    if (a.sel_asc)
+      for (int i = tid; i < k; i += BLOCK) a.sel_asc[(int64_t)r * k + i] = -1;
     if (a.n_sel && tid == 0) a.n_sel[r] = 0;
     return;
   }
@@ -376,19 +378,60 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     bucketed[atomicAdd(&hist[(int)((key - thresh) >> shb)], 1)] = key;
   }
   __syncthreads();
-  // Place of an element = its bucket's offset + larger keys in the bucket;
-  // the first nsel places are the selection, in order.
+  // Ascending order (optional): the winners' rows are marked in a bitmap of
+  // the visible rows (nv <= kMaxComp bits) laid over keys[], which is free
+  // once scattered, and read back in row order after a block-wide scan of
+  // the words' popcounts.
+  unsigned* const bits = reinterpret_cast<unsigned*>(keys);
+  const int nwords = (nv + 31) >> 5;
+  if (a.sel_asc) {
+    for (int i = tid; i < nwords; i += BLOCK) bits[i] = 0u;
+    __syncthreads();
+  }
+  // Place of an element = its bucket's start + larger keys in the bucket; the
+  // first nsel places are the selection, in order. After the scatter hist[b]
+  // is the end of bucket b, and the end of the bucket above (placed before
+  // it) is its start.
   for (int p = tid; p < n_coll; p += BLOCK) {
     const u64 key = bucketed[p];
     const int b = (int)((key - thresh) >> shb);
-    // After the scatter hist[b] is the end of bucket b, and the end of the
-    // bucket above (placed before it) is its start.
     const int st = b + 1 < kBins1 ? hist[b + 1] : 0, en = hist[b];
     int place = st;
     for (int q = st; q < en; ++q) place += bucketed[q] > key ? 1 : 0;
-    if (place < nsel) sel_row[place] = (nv - 1) - (int)(key & emask);
+    if (place < nsel) {
+      const int row = (nv - 1) - (int)(key & emask);
+      sel_row[place] = row;
+      if (a.sel_asc) atomicOr(&bits[row >> 5], 1u << (row & 31));
+    }
   }
   for (int i = nsel + tid; i < k; i += BLOCK) sel_row[i] = -1;
+  if (a.sel_asc) {
+    __syncthreads();
+    const int wpt = (nwords + BLOCK - 1) / BLOCK;  // words per thread, consecutive
+    int cnt = 0;
+    for (int i = 0; i < wpt; ++i) {
+      const int w = tid * wpt + i;
+      if (w < nwords) cnt += __popc(bits[w]);
+    }
+    const int incl = wave_incl_scan(cnt, lane);
+    if (lane == 63) red_a[wave] = incl;
+    __syncthreads();
+    int pos = incl - cnt;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) pos += w < wave ? red_a[w] : 0;
+    int32_t* asc_row = a.sel_asc + (int64_t)r * k;
+    for (int i = 0; i < wpt; ++i) {
+      const int w = tid * wpt + i;
+      if (w < nwords) {
+        unsigned m = bits[w];
+        while (m) {
+          asc_row[pos++] = 32 * w + (__ffs(m) - 1);
+          m &= m - 1;
+        }
+      }
+    }
+    for (int i = nsel + tid; i < k; i += BLOCK) asc_row[i] = -1;
+  }
   if (a.n_sel && tid == 0) a.n_sel[r] = nsel;
 }
 
@@ -490,6 +533,7 @@ hipError_t launch_fused_topk(const FusedArgs& f, hipStream_t stream) {
   TopkArgs a{};
   a.sel = f.sel;
   a.n_sel = f.n_sel;
+  a.sel_asc = f.sel_asc;
   a.n_q = f.n_q;
   a.q_pos0 = f.q_pos0;
   a.n_comp = f.n_comp;

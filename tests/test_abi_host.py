@@ -108,7 +108,7 @@ def test_workspace_bytes():
     w = workloads.PREFILL_8192
     d = desc_of(w)
     nb = sp.spmla_prefill_workspace_bytes(d)
-    assert nb == 2048 * 2048 * 4 + 2048 * 512 * 4
+    assert nb == 2048 * 2048 * 4 + 2 * 2048 * 512 * 4  # scores + selections in two orders
     w4 = workloads.CHUNK_8192_AT_114687
     nb4 = sp.spmla_prefill_workspace_bytes(desc_of(w4))
     assert nb4 >= 2048 * 30719 * 4 + 2048 * 2048 * 4
@@ -130,7 +130,7 @@ def test_workspace_covers_split_partials_and_fused_candidates():
     n_spans = -(-w.n_comp // 512)
     assert nb >= 2048 * n_spans * 128 * 8 + 2048 * n_spans * 4  # candidate slots + counts
     # a call too large for splits needs no partials: the dense band dominates
-    assert sp.spmla_prefill_workspace_bytes(desc_of(workloads.PREFILL_8192)) == 2048 * 2048 * 4 + 2048 * 512 * 4
+    assert sp.spmla_prefill_workspace_bytes(desc_of(workloads.PREFILL_8192)) == 2048 * 2048 * 4 + 2 * 2048 * 512 * 4
 
 
 A = 1 << 20  # an aligned fake address; never dereferenced by these calls
