@@ -26,6 +26,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix
 METRIC = "sparse-MLA prefill tokens/s per layer; % of HBM/MFMA roofline"
+# spmla_prefill hands the attention each selection in ascending row order when
+# the compressed rows (576 fp16 each) exceed one die's L2.
+ASCENDING_ROWS_ABOVE_BYTES = 4 << 20
+
+
+def attn_order(torch, sel_rows, ascending):
+    """The selection as spmla_prefill passes it to the attention: score order,
+    or rows ascending with the -1 padding last."""
+    if not ascending:
+        return sel_rows.contiguous()
+    big = torch.iinfo(torch.int32).max
+    s = torch.sort(torch.where(sel_rows < 0, big, sel_rows), dim=1).values
+    return torch.where(s == big, -1, s).contiguous()
 ATTN_SRC = os.path.join(ROOT, "sparse_long_context_int8_amd", "csrc", "attn.hip")
 
 
@@ -147,14 +160,16 @@ def bench_compress(args, sp, workloads, torch):
 
 def bench_attn_grouped(args, sp, workloads, torch):
     """Streaming (spmla_sparse_attn) against query-tiled (grouped) attention,
-    band by band on the selections spmla_prefill made, as the pages compare
-    their grouped and streaming kernels."""
+    band by band on the selections spmla_prefill made (in the order it hands
+    them to its attention), as the pages compare their grouped and streaming
+    kernels."""
     w = workloads.BY_NAME[args.workload]
     log(f"attn-grouped {w.name}: generating inputs")
     x = workloads.generate(w)
     dev = {k: torch.from_numpy(v).cuda() for k, v in x.items()}
     desc = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
     out, lse, sel = sp.prefill(desc, dev)
+    sel = attn_order(torch, sel, w.n_comp * w.d_qk * 2 > ASCENDING_ROWS_ABOVE_BYTES)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     n_bands = sp.spmla_num_bands(desc)
@@ -270,8 +285,11 @@ def main():
     value = w.n_q * args.steps / (total_ms / 1e3)
 
     # Per-kernel launch durations, same launch configuration (one band per
-    # launch) on the same stream, HIP events between the launches.
+    # launch) on the same stream, HIP events between the launches. The
+    # attention gets its selection in the order spmla_prefill hands it over:
+    # ascending rows once the compressed rows outgrow one die's L2.
     log("per-kernel breakdown")
+    ascending = w.n_comp * w.d_qk * 2 > ASCENDING_ROWS_ABOVE_BYTES
     n_bands = sp.spmla_num_bands(desc)
     scores_b = torch.empty((min(w.band, w.n_q), w.n_comp), dtype=torch.int32, device="cuda")
     ev = {k: [] for k in ("indexer", "topk", "attn")}
@@ -282,22 +300,24 @@ def main():
             bn = min(w.band, w.n_q - a0)
             d = sp.make_desc(bn, w.q_pos0 + a0, w.window, w.top_k, ratio=w.ratio, band=w.band,
                              n_raw=w.n_raw)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             e[0].record()
             sp.spmla_indexer_scores(d, dev["iq"][a0:a0 + bn], dev["iw"][a0:a0 + bn], dev["ik"],
                                     scores_b[:bn])
             e[1].record()
             sp.spmla_topk(d, scores_b[:bn], sel[a0:a0 + bn])
             e[2].record()
-            sp.spmla_sparse_attn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"],
-                                 sel[a0:a0 + bn], out[a0:a0 + bn], lse[a0:a0 + bn])
+            attn_sel = attn_order(torch, sel[a0:a0 + bn], ascending)  # untimed preparation
             e[3].record()
+            sp.spmla_sparse_attn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"],
+                                 attn_sel, out[a0:a0 + bn], lse[a0:a0 + bn])
+            e[4].record()
             ev["indexer"].append(e)
     torch.cuda.synchronize()
     launches = ev["indexer"]
     t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in launches]))
     t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in launches]))
-    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in launches]))
+    t_attn = float(np.mean([e[3].elapsed_time(e[4]) for e in launches]))
 
     bytes_q = attn_bytes_per_query(w)
     flops_q = attn_flops_per_query(w)
@@ -352,6 +372,7 @@ def main():
         # prefill step spends per band outside attention.
         "abi_calls_ms_per_band": {"indexer_scores": round(t_idx, 4), "topk": round(t_topk, 4),
                                   "sparse_attn": round(t_attn, 4)},
+        "attn_rows_ascending": ascending,
         # Calls under 512 queries split each key list across workgroups inside
         # spmla_prefill (spmla_sparse_attn has no workspace and does not), so
         # the difference is only meaningful for larger calls.
