@@ -127,6 +127,13 @@ __device__ __forceinline__ unsigned long long lds_read_u64(unsigned addr) {
   return v;
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Waits until at most N LDS operations are outstanding (they complete in
+// issue order); N fits the 4-bit counter.
+template <int N>
+__device__ __forceinline__ void lds_wait_n() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
 template <typename T>
 __device__ __forceinline__ void fence_reg(T& v) {
   asm volatile("" : "+v"(v));
@@ -477,13 +484,18 @@ void attn_kernel(AttnArgs a) {
     const int tri = (lane >> 2) & 3;
     const int trc = lane & 3;
     // Streaming reads them before the S^T exchange (its buffer is refilled
-    // right after it); the pair variant, which refills only after the next
-    // chunk's barrier, reads them after the exchange (fewer live registers).
+    // right after it), in two halves issued behind the K fragments so that
+    // the first QK products need not wait for them; the pair variant, which
+    // refills only after the next chunk's barrier, reads them after the
+    // exchange (fewer live registers).
     constexpr bool kEarlyV = GROUP == 1;
+    constexpr int kNtHalf = C::kNt / 2;
+    constexpr int kVReadsHalf = kNtHalf * C::kPvSteps * kUnits;
     short4v vt[C::kNt][C::kPvSteps][kUnits];
-    auto read_v = [&]() {
+    auto read_v = [&](int nt_begin, int nt_end) {
 #pragma unroll
       for (int nt = 0; nt < C::kNt; ++nt) {
+        if (nt < nt_begin || nt >= nt_end) continue;
         const int dv0 = (kDv / WAVES) * wave + 16 * nt;
         const int unit = (dv0 >> 3) + (trc >> 1);
         const int sub = (trc & 1) << 3;
@@ -504,9 +516,7 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int u = 0; u < kUnits; ++u) fence_reg(vt[nt][kb][u]);
     };
-    if constexpr (kEarlyV) read_v();
     unsigned long long valid = valid_in;
-    if constexpr (GROUP == 1) valid = lds_read_u64(valid_lds);
 
     // The contraction slice is a compile-time constant inside qk(), so each
     // K read address is fixed at compile time (no per-read branches).
@@ -515,9 +525,12 @@ void attn_kernel(AttnArgs a) {
       const int n = 16 * tile + c16;
       constexpr int kLen = C::len(HALF);
       constexpr int kStart = C::start(HALF);
-      // K fragments in two batches (fewer live registers); the first wait
-      // also covers the V^T and mask reads issued before.
+      // K fragments in two batches (fewer live registers). Streaming issues
+      // the first half of its V^T reads behind the second batch and waits
+      // only for that batch; the rest of V^T and the chunk's validity mask
+      // follow the products, and the exchange barrier's wait covers them.
       constexpr int kBatch = (kLen + 1) / 2;
+      static_assert(kLen > kBatch, "two K batches");
       auto read_k = [&](half8(&kf)[kBatch], int s0, int cnt) {
 #pragma unroll
         for (int s = 0; s < kBatch; ++s) {
@@ -539,28 +552,39 @@ void attn_kernel(AttnArgs a) {
         lds_wait();
 #pragma unroll
         for (int s = 0; s < kBatch; ++s) fence_reg(kf[s]);
-        if constexpr (kEarlyV) fence_v();
-        fence_reg(valid);
 #pragma unroll
         for (int s = 0; s < kBatch; ++s)
           sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], sacc[s % 3], 0, 0, 0);
       }
-      if constexpr (kLen > kBatch) {
+      {
         half8 kf[kBatch];
         read_k(kf, kBatch, kLen - kBatch);
-        lds_wait();
+        if constexpr (kEarlyV) {
+          read_v(0, kNtHalf);
+          lds_wait_n<kVReadsHalf>();
+        } else {
+          lds_wait();
+        }
 #pragma unroll
         for (int s = 0; s < kLen - kBatch; ++s) fence_reg(kf[s]);
 #pragma unroll
         for (int s = kBatch; s < kLen; ++s)
           sacc[s % 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s - kBatch], qf[s], sacc[s % 3], 0, 0, 0);
       }
+      if constexpr (kEarlyV) {
+        read_v(kNtHalf, C::kNt);
+        valid = lds_read_u64(valid_lds);
+      }
       const float4v ssum = (sacc[0] + sacc[1]) + sacc[2];
       const int slot = s_slot<CHUNK>(4 * tile + g, c16);
       *reinterpret_cast<float4v*>(&sbuf_c[(HALF * kHeads + c16) * C::kSStride + 4 * slot]) = ssum;
     };
     with_slice<C::kHalves>(half, qk);
-    lds_barrier();
+    lds_barrier();  // also completes this wave's V^T and mask reads
+    if constexpr (kEarlyV) {
+      fence_v();
+      fence_reg(valid);
+    }
 
     // Online softmax for head c16 over keys kPvKeys*kb + kKpl*g + i. The S^T
     // reads are issued before after_exchange(), whose own LDS wait covers them.
@@ -576,7 +600,7 @@ void attn_kernel(AttnArgs a) {
           sp[kb][hh][u] = lds_read_f4(srow + 16u * su);
         }
       }
-    if constexpr (!kEarlyV) read_v();
+    if constexpr (!kEarlyV) read_v(0, C::kNt);
     after_exchange();
     lds_wait();
     if constexpr (!kEarlyV) fence_v();
