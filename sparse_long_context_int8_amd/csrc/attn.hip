@@ -443,17 +443,15 @@ void attn_kernel(AttnArgs a) {
     return p;
   };
   // This wave's share of the gather of one chunk: kRowsPerHw value loads
-  // (one row each, row n's pointer in lane n of kp) and one rope load
-  // covering the same rows (lane l loads part of row row0 + l/8, whose
-  // pointer it holds in kr).
+  // (one row each, row n's pointer in lane n of kp = (kp_hi, kp_lo)), here
+  // rows [i0, i1) of them, and one rope load covering the same rows (lane l
+  // loads part of row row0 + l/8, whose pointer it holds in kr).
   const int row0 = hw * kRowsPerHw;
   const int rope_row = row0 + min(lane >> 3, kRowsPerHw - 1);
-  auto gather = [&](const char* kp, const char* kr, lds_char* buf) {
-    const uintptr_t kpi = (uintptr_t)kp;
-    const unsigned kp_lo = (unsigned)kpi;
-    const unsigned kp_hi = (unsigned)(kpi >> 32);
+  auto gather_rows = [&](unsigned kp_lo, unsigned kp_hi, lds_char* buf, int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < kRowsPerHw; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int n = row0 + i;
       const unsigned lo = __builtin_amdgcn_readlane(kp_lo, n);
       const unsigned hi = __builtin_amdgcn_readlane(kp_hi, n);
@@ -461,6 +459,8 @@ void attn_kernel(AttnArgs a) {
       const unsigned off = (unsigned)(lane ^ swz_a(n)) << 4;  // zero-extended: SGPR base + VGPR offset form
       __builtin_amdgcn_global_load_lds((gbl_char*)(rowp + off), buf + n * 1024, 16, 0, 0);
     }
+  };
+  auto gather_rope = [&](const char* kr, lds_char* buf) {
     lds_char* const rope_dst = buf + C::kBufA + row0 * 128;
     if (lane < 8 * kRowsPerHw) {
       const int off = (64 + ((lane & 7) ^ swz_b(rope_row))) << 4;
@@ -468,13 +468,14 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // One chunk in `cur`. All LDS reads of the chunk (this wave's K and V^T
-  // fragments, and for streaming its validity mask) are issued together and
-  // waited for once; after the S^T exchange barrier `cur` is no longer read,
-  // and after_exchange() may start refilling it. No barrier is needed at the
-  // end of a chunk: the S^T area is written again only after a later chunk's
-  // barrier, which every wave reaches after its last read of it.
-  auto compute = [&](lds_char* cur, unsigned long long valid_in, unsigned valid_lds, int sb, auto&& after_exchange) {
+  // One chunk in `cur`. After the S^T exchange barrier `cur` is no longer
+  // read, and stage(0) .. stage(4) may refill it: stage 0 is called right
+  // after the S^T reads are issued (before their wait), stages 1-4 between
+  // the steps of the softmax, so that the loads of the next gather reach the
+  // memory pipeline spread out rather than in one burst. No barrier is
+  // needed at the end of a chunk: the S^T area is written again only after a
+  // later chunk's barrier, which every wave reaches after its last read of it.
+  auto compute = [&](lds_char* cur, unsigned long long valid_in, unsigned valid_lds, int sb, auto&& stage) {
     const unsigned bA = (unsigned)(uintptr_t)cur;  // LDS byte address
     float* sbuf_c = sbuf_g + sb * (C::kSBytes / 4);
     const unsigned sbuf_c_addr = sbuf_addr + sb * C::kSBytes;
@@ -601,7 +602,7 @@ void attn_kernel(AttnArgs a) {
         }
       }
     if constexpr (!kEarlyV) read_v(0, C::kNt);
-    after_exchange();
+    stage(std::integral_constant<int, 0>{});
     lds_wait();
     if constexpr (!kEarlyV) fence_v();
     float zz[C::kPvSteps][kKpl];
@@ -616,6 +617,8 @@ void attn_kernel(AttnArgs a) {
           for (int i = 0; i < 4; ++i)
             zz[kb][4 * u + i] = hh == 0 ? sp[kb][hh][u][i] : zz[kb][4 * u + i] + sp[kb][hh][u][i];
         }
+    stage(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
     // Keys past the end of the list (or rejected indices) only occur in
     // chunks that are not entirely valid.
     const unsigned vlo = __builtin_amdgcn_readfirstlane((unsigned)valid);
@@ -636,6 +639,12 @@ void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < C::kPvSteps; ++kb)
 #pragma unroll
       for (int i = 0; i < kKpl; ++i) cmax = fmaxf(cmax, zz[kb][i]);
+    // The fences pin each step's results ahead of the next stage's loads
+    // (the compiler would otherwise sink the arithmetic to its uses).
+    fence_reg(cmax);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(std::integral_constant<int, 2>{});
+    __builtin_amdgcn_sched_barrier(0);
     cmax = max4_heads(cmax) * a.scale_log2e;  // scale > 0, so the max commutes with it
     // Move the reference (and rescale O and l) only when needed; the test is
     // made per head and the branch is taken if any head needs it.
@@ -647,7 +656,11 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] *= alpha;
     }
-    const float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+    float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+    fence_reg(m_use);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
     using pvec = std::conditional_t<kKpl == 8, half8, half4>;
     pvec pf[C::kPvSteps];
     float psum = 0.f;
@@ -660,6 +673,12 @@ void attn_kernel(AttnArgs a) {
         pf[kb][i] = (_Float16)p;
       }
     l_run += psum;
+#pragma unroll
+    for (int kb = 0; kb < C::kPvSteps; ++kb) fence_reg(pf[kb]);
+    fence_reg(l_run);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(std::integral_constant<int, 4>{});
+    __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T . P^T
 #pragma unroll
@@ -701,20 +720,47 @@ void attn_kernel(AttnArgs a) {
   if constexpr (GROUP == 1) {
     auto buf_of = [&](int ch) { return bufs + ((unsigned)ch % NBUF) * C::kBuf; };
     // Gather of chunk ch into its ring buffer and its validity mask into its
-    // slot; its selected indices are already in LDS.
-    auto issue = [&](int ch) {
+    // slot; its selected indices are already in LDS. Split into the stages
+    // of compute(): 0 reads the indices, 1 forms the row pointers, the mask
+    // and the first rows' loads, 2-4 the remaining loads (4 also the rope
+    // load and the index load of chunk ch + NBUF + 1).
+    constexpr int kRowsPerStage = (kRowsPerHw + 3) / 4;
+    int s_main = 0, s_rope = 0;
+    unsigned kp_lo = 0, kp_hi = 0;
+    const char* kr = self_row;
+    auto issue_stage = [&](int ch, auto st_c) {
+      constexpr int ST = decltype(st_c)::value;
       const int slot = (int)((unsigned)ch % C::kSlots);
-      int s_main = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + min(lane, CHUNK - 1)));
-      int s_rope = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + rope_row));
+      if constexpr (ST == 0) {
+        s_main = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + min(lane, CHUNK - 1)));
+        s_rope = lds_read_i32(sel_ring_addr + 4u * (slot * CHUNK + rope_row));
+      } else {
+        if constexpr (ST == 1) {
+          fence_reg(s_main);
+          fence_reg(s_rope);
+          bool ok, ok_rope;
+          const char* kp = row_ptr(ch * CHUNK + lane, s_main, ok);
+          kr = row_ptr(ch * CHUNK + rope_row, s_rope, ok_rope);
+          kp_lo = (unsigned)(uintptr_t)kp;
+          kp_hi = (unsigned)((uintptr_t)kp >> 32);
+          const unsigned long long vm = __ballot(ok && lane < CHUNK);
+          if (hw == 0 && lane == 0) valid_slots[slot] = vm;
+        }
+        gather_rows(kp_lo, kp_hi, buf_of(ch), (ST - 1) * kRowsPerStage, ST * kRowsPerStage);
+        if constexpr (ST == 4) {
+          gather_rope(kr, buf_of(ch));
+          load_sel(ch + NBUF + 1);
+        }
+      }
+    };
+    // The whole gather at once (prologue).
+    auto issue = [&](int ch) {
+      issue_stage(ch, std::integral_constant<int, 0>{});
       lds_wait();
-      fence_reg(s_main);
-      fence_reg(s_rope);
-      bool ok, ok_rope;
-      const char* kp = row_ptr(ch * CHUNK + lane, s_main, ok);
-      const char* kr = row_ptr(ch * CHUNK + rope_row, s_rope, ok_rope);
-      const unsigned long long vm = __ballot(ok && lane < CHUNK);
-      if (hw == 0 && lane == 0) valid_slots[slot] = vm;
-      gather(kp, kr, buf_of(ch));
+      issue_stage(ch, std::integral_constant<int, 1>{});
+      issue_stage(ch, std::integral_constant<int, 2>{});
+      issue_stage(ch, std::integral_constant<int, 3>{});
+      issue_stage(ch, std::integral_constant<int, 4>{});
     };
     // Prologue: Q fragments and the indices of the first NBUF+1 chunks, all
     // waited for; then the gathers of the first NBUF chunks, each followed by
@@ -728,10 +774,7 @@ void attn_kernel(AttnArgs a) {
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) {
-      if (c_begin + k < c_end) {
-        issue(c_begin + k);
-        load_sel(c_begin + k + NBUF + 1);
-      }
+      if (c_begin + k < c_end) issue(c_begin + k);  // includes the index load NBUF + 1 chunks ahead
     }
     for (int ch = c_begin; ch < c_end; ++ch) {
       // Chunk ch's loads (and all before them) are complete once at most
@@ -740,11 +783,9 @@ void attn_kernel(AttnArgs a) {
       if (ch + NBUF - 1 < c_end) wait_vmcnt<C::kWaitAhead>();
       else wait_vmcnt<0>();
       lds_barrier();
-      compute(buf_of(ch), 0ull, valid_addr + 8u * ((unsigned)ch % C::kSlots), 0, [&]() {
-        if (ch + NBUF < c_end) {
-          issue(ch + NBUF);
-          load_sel(ch + 2 * NBUF + 1);
-        }
+      const bool refill = ch + NBUF < c_end;  // uniform
+      compute(buf_of(ch), 0ull, valid_addr + 8u * ((unsigned)ch % C::kSlots), 0, [&](auto st_c) {
+        if (refill) issue_stage(ch + NBUF, st_c);
       });
     }
     wait_vmcnt<0>();  // index loads for chunks past the end
@@ -760,7 +801,8 @@ void attn_kernel(AttnArgs a) {
       const unsigned lo = __shfl((unsigned)kpi, rope_row);
       const unsigned hi = __shfl((unsigned)(kpi >> 32), rope_row);
       const unsigned long long vm = __ballot(ok);
-      gather(kp, reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo), buf);
+      gather_rows((unsigned)kpi, (unsigned)(kpi >> 32), buf, 0, kRowsPerHw);
+      gather_rope(reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo), buf);
       return vm;
     };
     unsigned long long valid_cur = gather_pair(c_begin, buf0);
@@ -770,7 +812,7 @@ void attn_kernel(AttnArgs a) {
       lds_barrier();
       unsigned long long valid_next = 0;
       if (ch + 1 < c_end) valid_next = gather_pair(ch + 1, nxt);
-      compute(cur, valid_cur, 0u, ch & 1, [] {});
+      compute(cur, valid_cur, 0u, ch & 1, [](auto) {});
       valid_cur = valid_next;
     };
     for (int ch = c_begin;;) {
