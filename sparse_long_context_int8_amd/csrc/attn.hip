@@ -7,16 +7,17 @@
 // uses a fast exponential. Here: fp16 operands on matrix cores, fp32
 // accumulation and softmax, exp2 with log2(e) folded into the scale.
 //
-// One workgroup per query token. Its key list is the selected compressed
-// rows followed by the sliding-window raw rows; keys stream through LDS in
-// chunks of CHUNK rows gathered with direct global->LDS loads, so each row
-// crosses the memory system once per query.
+// One workgroup per query token (or per key split of one). Its key list is
+// the selected compressed rows followed by the sliding-window raw rows; keys
+// stream through a ring of LDS buffers in chunks of CHUNK rows gathered with
+// direct global->LDS loads, so each row crosses the memory system once per
+// query.
 //
 // LDS image of a chunk (per buffer):
 //   region A: CHUNK rows x 1024 B = latent dims 0..511 (the value part),
 //             one wave-wide 16-byte-per-lane load per row;
 //   region B: CHUNK rows x 128 B  = latent dims 512..575 (the rope part),
-//             one load per 8 rows.
+//             one load per wave covering its rows.
 // 16-byte units are XOR-swizzled per row so that the K reads (16 rows x 16 B
 // per pass) and the transposed V reads (8 rows x 32 B per pass) hit distinct
 // banks.
@@ -30,8 +31,10 @@
 //       lane-local;
 //   PV: O^T[512/W dims x 16 heads] += V^T . P^T per wave, V^T fragments read
 //       with ds_read_b64_tr_b16 (the gfx950 transpose load) from the
-//       row-major region A, P^T built in registers.
-// With NBUF == 2 the gather of chunk i+1 is in flight while chunk i computes.
+//       row-major region A before the exchange, P^T built in registers.
+// A chunk's buffer is refilled right after the exchange (the gather of the
+// chunk NBUF places later), so NBUF gathers are in flight while softmax and
+// PV run.
 #include "spmla_internal.h"
 
 #include <type_traits>
@@ -99,8 +102,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // compiler's wait insertion would otherwise treat every read of one buffer
 // as possibly depending on the global->LDS loads still landing in the other
 // buffer and wait for all of them (vmcnt(0)), which serializes the gather
-// pipeline. Each group of reads ends with lds_wait() and fence_reg() on the
-// results, so no value is used before it has arrived.
+// pipeline. Each group of reads is followed by an lgkmcnt wait (lds_wait,
+// lds_wait_n or the barrier's) and fence_reg() on the results, so no value
+// is used before it has arrived.
 __device__ __forceinline__ half8 lds_read_b128(unsigned addr) {
   half8 v;
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
@@ -233,9 +237,10 @@ constexpr float kRescaleThreshold = 8.0f;
 
 // GROUP == 1: streaming, one (query, key split) per workgroup of WAVES
 // waves, keys through a ring of NBUF chunk buffers. A chunk's buffer is read
-// (K and V^T fragments into registers) before its S^T exchange barrier; right
-// after that barrier the gather of the chunk NBUF places later is issued into
-// it, so NBUF gathers are in flight while softmax and PV run. The selected
+// (K and V^T fragments into registers) before its S^T exchange barrier; after
+// that barrier the gather of the chunk NBUF places later is issued into it,
+// in stages between the softmax steps, so NBUF gathers are in flight while
+// softmax and PV run. The selected
 // indices arrive by the same global->LDS path ahead of their gather, so the
 // loop issues no other global load and each wave's only memory wait is a
 // vmcnt that lets the later chunks' loads stay outstanding (loads complete
