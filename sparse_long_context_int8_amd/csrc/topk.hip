@@ -34,7 +34,7 @@ typedef unsigned long long u64;
 
 constexpr int kBins1 = 2048;  // coarse-pass and ordering bins (11 bits)
 constexpr int kBits1 = 11;
-constexpr int kSlack = 512;  // elements beyond k a workgroup may collect and order
+constexpr int kSlack = 256;  // elements beyond k a workgroup may collect and order
 
 // Wave-wide scans and reductions with DPP (no LDS round trips): row_shr:n
 // shifts within each 16-lane row (lanes without a source take the identity),
