@@ -34,7 +34,10 @@ typedef unsigned long long u64;
 
 constexpr int kBins1 = 2048;  // coarse-pass and ordering bins (11 bits)
 constexpr int kBits1 = 11;
-constexpr int kSlack = 256;  // elements beyond k a workgroup may collect and order
+// Elements beyond k a workgroup may collect and order. With top_k 512 over
+// at most 2,048 rows a workgroup then holds 8,256 + 12,032 B of LDS, under
+// 20 KiB, so eight share a CU and a 2,048-token band runs in one round.
+constexpr int kSlack = 240;
 
 // Wave-wide scans and reductions with DPP (no LDS round trips): row_shr:n
 // shifts within each 16-lane row (lanes without a source take the identity),
@@ -138,6 +141,9 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   __shared__ int red_a[NW], red_b[NW], red_c[NW];
   __shared__ int s_bin, s_above, s_count, s_cnt;
   __shared__ int aux[BLOCK + 1];  // span offsets (candidates) or the query row (recompute)
+  // Candidates: the span of each collected slot (spans < 256).
+  __shared__ unsigned char span_of[SRC == kCandidate ? BLOCK * PER : 1];
+  static_assert(SRC != kCandidate || BLOCK <= 256, "span indices fit a byte");
   extern __shared__ u64 keys[];
 
   const int tid = threadIdx.x;
@@ -229,6 +235,10 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
       if (tid == 0) f.redo_list[atomicAdd(f.n_redo, 1)] = r;
       return;
     }
+    // Slots [aux[s], aux[s] + held) are span s's; label each with its span so
+    // that an element finds its span with one LDS read.
+    if (tid < ns)
+      for (int e = aux[tid], e1 = aux[tid] + held; e < e1; ++e) span_of[e] = (unsigned char)tid;
     __syncthreads();
     n_el = total;
     const int32_t* cand_row = f.cand + 2 * ((int64_t)r * ns * cap);
@@ -238,12 +248,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
       sc[i] = INT32_MIN;
       jx[i] = 0;
       if (e < n_el) {
-        int lo = 0, hi = ns - 1;  // last span whose offset is <= e
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (aux[mid] <= e) lo = mid;
-          else hi = mid - 1;
-        }
+        const int lo = span_of[e];
         const int2 c = *reinterpret_cast<const int2*>(cand_row + 2 * ((int64_t)lo * cap + (e - aux[lo])));
         sc[i] = c.x;
         jx[i] = c.y;
@@ -397,7 +402,16 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     const int b = (int)((key - thresh) >> shb);
     const int st = b + 1 < kBins1 ? hist[b + 1] : 0, en = hist[b];
     int place = st;
-    for (int q = st; q < en; ++q) place += bucketed[q] > key ? 1 : 0;
+    // Four bucket entries per step (independent reads; most buckets hold
+    // only a few keys).
+    for (int q = st; q < en; q += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = q + j < en;
+        const u64 o = in ? bucketed[q + j] : 0ull;
+        place += (in && o > key) ? 1 : 0;
+      }
+    }
     if (place < nsel) {
       const int row = (nv - 1) - (int)(key & emask);
       sel_row[place] = row;
