@@ -22,7 +22,7 @@
 //      (buckets hold a few keys for spread-out scores); the first k places
 //      are the output.
 // The refinement (2) runs only while the keys at or above the threshold
-// would exceed k + 512; usually the coarse bin already gets there, and its
+// would exceed k + kSlack; usually the coarse bin already gets there, and its
 // extra keys simply fall beyond place k.
 // Integer only: exact, and independent of thread timing.
 #include "spmla_internal.h"
