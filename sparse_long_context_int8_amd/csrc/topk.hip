@@ -139,7 +139,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   constexpr int NW = BLOCK / 64;
   __shared__ int hist[kBins1];
   __shared__ int red_a[NW], red_b[NW], red_c[NW];
-  __shared__ int s_bin, s_above, s_count, s_cnt;
+  __shared__ int s_bin, s_above, s_count;
   __shared__ int aux[BLOCK + 1];  // span offsets (candidates) or the query row (recompute)
   // Candidates: the span of each collected slot (spans < 256).
   __shared__ unsigned char span_of[SRC == kCandidate ? BLOCK * PER : 1];
@@ -345,38 +345,44 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   }
 
   // 3. Collect the elements >= thresh (at most cap, at least nsel) into
-  // keys[0 ..) (one LDS atomic per wave and register, lanes take consecutive
-  // slots) and count them per ordering bucket: the top 11 bits of
-  // (key - thresh); no key exceeds key_hi.
+  // keys[0 ..): each thread's count, one block-wide prefix scan, then every
+  // thread writes its keys to consecutive slots; and count them per ordering
+  // bucket: the top 11 bits of (key - thresh); no key exceeds key_hi.
   const u64 key_hi = ((u64)span << ebits) | emask;
   const u64 kspan = key_hi - thresh;
   const int kbits = kspan ? 64 - __clzll(kspan) : 0;
   const int shb = kbits > kBits1 ? kbits - kBits1 : 0;
   __syncthreads();
-  if (tid == 0) s_cnt = 0;
   for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += (i * BLOCK + tid < n_el && key_of(i) >= thresh) ? 1 : 0;
+  const int mine_incl = wave_incl_scan(mine, lane);
+  if (lane == 63) red_a[wave] = mine_incl;
   __syncthreads();
-  const u64 below = (1ull << lane) - 1;
+  int pos = mine_incl - mine, n_taken = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    pos += w < wave ? red_a[w] : 0;
+    n_taken += red_a[w];
+  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int e = i * BLOCK + tid;
-    const bool take = e < n_el && key_of(i) >= thresh;
-    const u64 m = __ballot(take);
-    if (m == 0) continue;  // wave-uniform
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&s_cnt, __popcll(m));
-    base = __builtin_amdgcn_readlane(base, 0);  // every lane is active here
-    const int pos = base + __popcll(m & below);
-    if (take && pos < cap) {  // pos < cap by construction
+    if (i * BLOCK + tid < n_el) {
       const u64 key = key_of(i);
-      keys[pos] = key;
-      atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+      if (key >= thresh) {
+        if (pos < cap) {  // by construction
+          keys[pos] = key;
+          atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+        }
+        ++pos;
+      }
     }
   }
   __syncthreads();
 
   bucket_offsets<BLOCK>(hist, red_c);
-  const int n_coll = min(s_cnt, cap);
+  const int n_coll = min(n_taken, cap);
   u64* bucketed = keys + cap;
   for (int e = tid; e < n_coll; e += BLOCK) {
     const u64 key = keys[e];
