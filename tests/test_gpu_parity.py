@@ -300,6 +300,35 @@ def test_band_invariant_long_history(sp):
     assert_close(np.array(got), np.array(want), "long-history rows vs oracle")
 
 
+@pytest.mark.parametrize("case", ["short-history", "long-history"])
+def test_optional_outputs_may_be_null(sp, case):
+    """spmla_prefill without sel_out (the selection then lives only in the
+    workspace) and without lse gives the same out, bit for bit. The long
+    history takes the fused selection and the ascending-row handoff."""
+    import torch
+
+    if case == "short-history":
+        w, seed = workloads.LayerShape("opt-short", n_q=700, q_pos0=3000, window=128, top_k=512, band=300), 12
+    else:
+        w, seed = workloads.LayerShape("opt-long", n_q=300, q_pos0=110000, window=128, top_k=2048), 13
+    say(f"[parity] null sel/lse outputs, {w.name}: n_q={w.n_q} q_pos0={w.q_pos0} band={w.band}")
+    x = workloads.generate(w, seed=seed)
+    dev = to_dev(x)
+    o1, l1, s1 = sp.prefill(desc_of(sp, w), dev)
+    o2, l2, s2 = sp.prefill(desc_of(sp, w), dev, want_sel=False, want_lse=False)
+    o3, l3, s3 = sp.prefill(desc_of(sp, w), dev, want_sel=False)
+    torch.cuda.synchronize()
+    assert l2 is None and s2 is None and s3 is None
+    assert torch.equal(o1, o2), "out differs without sel/lse"
+    assert torch.equal(o1, o3), "out differs without sel"
+    assert torch.equal(l1, l3), "lse differs without sel"
+    r = w.n_q - 1
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k, scale=w.scale,
+                         d_v=w.d_v, q_begin=r, q_end=r + 1)
+    np.testing.assert_array_equal(s1[r].cpu().numpy(), ref["sel"][0])
+    assert_close(o2[r].cpu().numpy(), ref["out"][0], f"{w.name} last row vs oracle")
+
+
 def test_first_query_is_its_own_row(sp):
     """Query 0 sees one key (its own raw row): softmax weight exactly 1."""
     import torch
