@@ -93,12 +93,25 @@ def cpu_baseline(w, x):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import oracle  # test infrastructure: used only for this baseline leg
 
+    blas = None
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in pools] or [1])
+        blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                         for p in pools if p.get("user_api") == "blas") or None
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     # Whole workload if it is the 8,192-token prefill (about 10-15 s on
     # 8-16 host cores); otherwise the first 1,024 queries of the last band.
     if w.n_q <= 8192 and w.q_pos0 == 0:
@@ -121,6 +134,8 @@ def cpu_baseline(w, x):
         "wall_s": round(wall, 3),
         "cpu_s": round(cpu, 3),
         "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model,
+        "blas": blas,
     }
 
 
