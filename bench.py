@@ -65,6 +65,22 @@ def attn_bytes_per_query(w):
             + w.n_heads * 4 + 4 * n_sel)
 
 
+def step_roofline(w, ms_per_step):
+    """Whole-step model of the prefill call: per query, its gathered rows
+    (1,152 B each), q (18,432 B), out (32,768 B), the selection written and
+    read (8 B x top_k) and its indexer inputs (260 B) at 8 TB/s, plus 512 int8
+    ops per visible compressed row at 5 POP/s; frac = model time / measured."""
+    t = w.q_pos0 + np.arange(w.n_q, dtype=np.int64)
+    n_vis = np.minimum(w.n_comp, (t + 1) // w.ratio)
+    n_sel, n_win = keys_per_query(w)
+    nbytes = float((w.d_qk * 2 * (n_sel + n_win)).sum()) + w.n_q * (
+        w.n_heads * w.d_qk * 2 + w.n_heads * w.d_v * 4 + 8 * w.top_k + 4 * 64 + 4)
+    ops = 512.0 * float(n_vis.sum())
+    t_roof_ms = (nbytes / 8.0e12 + ops / 5.0e15) * 1e3
+    return {"bytes": nbytes, "int8_ops": ops, "t_roof_ms": round(t_roof_ms, 4),
+            "frac": round(t_roof_ms / ms_per_step, 4)}
+
+
 def attn_flops_per_query(w):
     n_sel, n_win = keys_per_query(w)
     return 2.0 * w.n_heads * (w.d_qk + w.d_v) * (n_sel + n_win)
@@ -393,6 +409,7 @@ def main():
         # the difference is only meaningful for larger calls.
         "prefill_selection_ms_per_band": (round(ms_per_step / n_bands - t_attn, 4) if w.n_q >= 512 else None),
         "roofline": roofline,
+        "step_roofline": step_roofline(w, ms_per_step),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
