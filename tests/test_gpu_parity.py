@@ -375,6 +375,41 @@ def test_edge_cases(sp, name, w):
     assert_close(o2.cpu().numpy(), ref["out"], f"{name} prefill out")
 
 
+def random_shapes(n_small=12, n_large=4, seed=2024):
+    """Seeded random descriptors: 1-300 queries (key-split attention) and
+    513-900 queries (whole-query attention), positions up to 6,000, windows
+    1-200, top-k 1-700 and bands of 1-2,048 queries."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n_small + n_large):
+        n_q = int(rng.choice([1, 2, 5, 17, 64, 130, 255, 300])) if i < n_small else int(rng.choice([513, 640, 900]))
+        shapes.append(workloads.LayerShape(
+            f"rand{i}", n_q=n_q, q_pos0=int(rng.integers(0, 6000)), window=int(rng.choice([1, 3, 16, 64, 128, 200])),
+            top_k=int(rng.choice([1, 7, 32, 100, 512, 700])), band=int(rng.choice([1, 37, 128, 256, 2048]))))
+    return shapes
+
+
+RANDOM = random_shapes()
+
+
+@pytest.mark.parametrize("w", RANDOM, ids=[w.name for w in RANDOM])
+def test_random_shapes(sp, w):
+    """spmla_prefill on seeded random shapes against the oracle: every query's
+    selection bit-exact, out and lse within tolerance."""
+    import torch
+
+    say(f"[parity random] {w.name}: n_q={w.n_q} q_pos0={w.q_pos0} window={w.window} top_k={w.top_k} band={w.band}")
+    x = workloads.generate(w, seed=100)
+    dev = to_dev(x)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"{w.name} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"{w.name} lse")
+
+
 @pytest.mark.parametrize("case", ["zero-queries-on-even-tokens", "sample-misleading-keys"])
 def test_fused_selection_recompute_paths(sp, case):
     """Long history (256 tokens, each sees ~30K rows and keeps 2,048): the sampled
