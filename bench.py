@@ -1,8 +1,11 @@
 """Benchmark: sparse-MLA prefill tokens/s per layer on one MI355X.
 
 One step = one spmla_prefill call over the 8,192-token prefill workload
-(four 2,048-query bands: indexer -> top-k -> streaming attention per band),
-inputs resident in HBM. Prints one JSON line:
+(four 2,048-query bands: the selection of all four, then streaming attention
+band by band), inputs resident in HBM. The default 100 warm-up steps (about
+50 ms of GPU work) bring the GPU to its sustained clocks before the timed
+steps; after 5 warm-up steps a step still runs about 11% slower. Prints one
+JSON line:
   value      whole-job tokens/s over the timed steps
   roofline   the attention kernel (dominant) against the HBM roofline, with
              algorithmic bytes per launch and its live launch duration
@@ -237,8 +240,8 @@ def bench_attn_grouped(args, sp, workloads, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill-8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,

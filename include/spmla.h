@@ -126,7 +126,7 @@ int spmla_num_bands(const spmla_desc* desc);
  *   scores  int32 [n_q][n_comp]  (output; exact integers)
  *
  * Writes the full n_q x n_comp matrix: meant for tests and short calls;
- * spmla_prefill only ever holds one band of it.
+ * spmla_prefill holds at most 128 MiB of it (one selection group) at once.
  */
 int spmla_indexer_scores(const spmla_desc* desc, const int8_t* iq, const int8_t* iw,
                          const int8_t* ik, int32_t* scores, void* stream);
@@ -212,18 +212,26 @@ int spmla_compress(const spmla_desc* desc, const uint16_t* kv_raw, uint16_t* kv_
                    void* stream);
 
 /*
- * Workspace bytes spmla_prefill needs for this descriptor: one band of
- * indexer scores (or, when larger, the fused selection's candidate slots or
- * the key-split partials of a small call) plus two bands of selected rows
- * (score order, and ascending row order for the attention's gathers).
+ * Workspace bytes spmla_prefill needs for this descriptor: the indexer
+ * scores of one selection group (or, when larger, the fused selection's
+ * candidate slots for one band or the key-split partials of a small call)
+ * plus that group's selected rows twice (score order, and ascending row
+ * order for the attention's gathers). A selection group is the largest
+ * number of whole bands whose score matrix fits 128 MiB (at least one band;
+ * all of them when they fit).
  * Returns SPMLA_OK and writes *bytes, or an error code.
  */
 int spmla_prefill_workspace_bytes(const spmla_desc* desc, size_t* bytes);
 
 /*
- * Steps 1-4 for all n_q queries, band by band: for each band of `band`
- * queries, indexer -> top-k -> attention, all enqueued on `stream` with no
- * host round trip. Same inputs and outputs as the three calls above;
+ * Steps 1-4 for all n_q queries in bands of `band` queries, all enqueued on
+ * `stream` with no host round trip. Attention runs band by band. Selection
+ * either takes the score matrix, for a selection group of consecutive bands
+ * at once (one indexer and one top-k launch for all of the group's queries,
+ * before the group's first attention launch), or, for a band of at least
+ * 256 queries that each see more than 4,096 (and at least 8 * top_k)
+ * compressed rows, the fused handoff of that band alone, which never writes
+ * the score matrix. Same inputs and outputs as the three calls above;
  * sel_out (int32 [n_q][top_k]) and lse may be NULL. When the compressed
  * rows exceed 4 MiB the attention takes each selection in ascending row
  * order, so out and lse can differ from spmla_sparse_attn on sel_out in

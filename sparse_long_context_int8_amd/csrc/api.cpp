@@ -91,15 +91,34 @@ size_t sel_bytes_per_band(const spmla_desc* d) {
 }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Selection groups: consecutive bands whose selection takes the score matrix
+// (not the fused handoff) get one indexer launch and one top-k launch for
+// all their queries, as long as the group's scores fit this budget; the
+// attention still runs band by band. One launch per step instead of one per
+// band removes the ramp and tail of short, latency-bound launches.
+constexpr size_t kSelGroupBytes = (size_t)128 << 20;
+int64_t sel_group_rows(const spmla_desc* d) {
+  const int64_t band_rows = d->band < d->n_q ? d->band : d->n_q;
+  const size_t per_band = scores_bytes_per_band(d);
+  int64_t bands = per_band ? (int64_t)(kSelGroupBytes / per_band) : INT64_MAX / 2 / (band_rows > 0 ? band_rows : 1);
+  if (bands < 1) bands = 1;
+  const int64_t rows = bands * band_rows;
+  return rows < d->n_q ? rows : d->n_q;
+}
+size_t sel_bytes_per_group(const spmla_desc* d) {
+  return (size_t)sel_group_rows(d) * (size_t)d->top_k * sizeof(int32_t);
+}
+
 constexpr size_t kRowBytes = (size_t)spmla::kDqk * 2;  // one fp16 latent row
 constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator die
-// Per-band scratch, reused by the steps of a band in stream order: the score
-// band of the dense selection or the fused selection's thresholds, slot
-// counts and candidates, then the attention's key-split partials (small
-// bands only), whichever is largest.
+// Scratch reused by the steps in stream order: the score matrix of a
+// selection group or the fused selection's thresholds, slot counts and
+// candidates (one band), then the attention's key-split partials (small
+// calls only), whichever is largest. A group's scores are dead once its
+// top-k has run, before the first attention launch of the group.
 size_t band_scratch_bytes(const spmla_desc* d) {
   const int rows = d->band < d->n_q ? d->band : d->n_q;
-  size_t need = round_up(scores_bytes_per_band(d), 256);
+  size_t need = round_up((size_t)sel_group_rows(d) * (size_t)band_ld(d) * sizeof(int32_t), 256);
   const size_t fused = spmla::fused_workspace_bytes(rows, spmla::fused_plan(d->n_comp, d->top_k));
   const size_t part = round_up(spmla::attn_partial_bytes(rows, spmla::attn_splits(d->n_q)), 256);
   if (fused > need) need = fused;
@@ -248,7 +267,7 @@ int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (!bytes) return fail(SPMLA_EINVAL, "bytes is NULL");
-  *bytes = band_scratch_bytes(d) + 2 * round_up(sel_bytes_per_band(d), 256);
+  *bytes = band_scratch_bytes(d) + 2 * round_up(sel_bytes_per_group(d), 256);
   return ok();
 }
 
@@ -285,14 +304,34 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
   // sweep the rows together and share what they gather (the softmax does not
   // depend on the order of its keys).
   const bool ascending = (size_t)d->n_comp * kRowBytes > kDieL2Bytes;
-  int32_t* band_sel_asc = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d) + round_up(sel_bytes_per_band(d), 256));
+  int32_t* band_sel_asc = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d) + round_up(sel_bytes_per_group(d), 256));
+  const int64_t group_cap = sel_group_rows(d);
+  auto band_len = [&](int64_t b) { return (int)((d->n_q - b) < d->band ? (d->n_q - b) : d->band); };
+  auto fused_band = [&](int64_t b) {
+    return d->n_comp > 0 && spmla::fused_applies(band_len(b), d->q_pos0 + (int)b, d->n_comp, d->ratio, d->top_k);
+  };
 
+  // The current dense selection group covers queries [g0, g1); its
+  // selections start at band_sel / band_sel_asc (or sel_out + g0 * top_k).
+  int64_t g0 = 0, g1 = 0;
   for (int64_t b0 = 0; b0 < d->n_q; b0 += d->band) {
-    const int bn = (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band);
+    const int bn = band_len(b0);
     const int pos0 = d->q_pos0 + (int)b0;
-    int32_t* sel = sel_out ? sel_out + b0 * d->top_k : band_sel;
+    const bool fused = fused_band(b0);
+    const bool new_group = !fused && b0 >= g1;
+    if (new_group) {
+      // This band and the following ones that also take the score matrix,
+      // up to the group's row budget (whole bands: the budget is a multiple
+      // of the band unless it covers every query).
+      g0 = b0;
+      g1 = b0 + bn;
+      while (g1 < d->n_q && g1 - g0 < group_cap && !fused_band(g1)) g1 += band_len(g1);
+    }
+    const int64_t slot = fused ? 0 : b0 - g0;  // row of this band's selection in the workspace
+    int32_t* sel = sel_out ? sel_out + b0 * d->top_k : band_sel + slot * d->top_k;
+    int32_t* sel_asc = band_sel_asc + slot * d->top_k;
 
-    if (d->n_comp > 0 && spmla::fused_applies(bn, pos0, d->n_comp, d->ratio, d->top_k)) {
+    if (fused) {
       // Long history: indexer -> top-k handoff without the score band.
       spmla::FusedArgs fa{};
       fa.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
@@ -300,7 +339,7 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       fa.ik = ik;
       fa.sel = sel;
       fa.n_sel = nullptr;
-      fa.sel_asc = ascending ? band_sel_asc : nullptr;
+      fa.sel_asc = ascending ? sel_asc : nullptr;
       fa.n_q = bn;
       fa.q_pos0 = pos0;
       fa.n_comp = d->n_comp;
@@ -310,7 +349,8 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       spmla::fused_bind_workspace(fa, ws);
       rc = hip_status(spmla::launch_fused_topk(fa, st), "fused selection launch");
       if (rc) return rc;
-    } else {
+    } else if (new_group) {
+      const int gn = (int)(g1 - g0);
       if (d->n_comp > 0) {
         spmla::IndexerArgs ia;
         ia.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
@@ -318,7 +358,7 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
         ia.ik = ik;
         ia.scores = band_scores;
         ia.ld_scores = band_ld(d);
-        ia.n_q = bn;
+        ia.n_q = gn;
         ia.q_pos0 = pos0;
         ia.n_comp = d->n_comp;
         ia.ratio = d->ratio;
@@ -332,8 +372,8 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       ta.ld_scores = band_ld(d);
       ta.sel = sel;
       ta.n_sel = nullptr;
-      ta.sel_asc = ascending ? band_sel_asc : nullptr;
-      ta.n_q = bn;
+      ta.sel_asc = ascending ? sel_asc : nullptr;
+      ta.n_q = gn;
       ta.q_pos0 = pos0;
       ta.n_comp = d->n_comp;
       ta.ratio = d->ratio;
@@ -342,7 +382,7 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
       if (rc) return rc;
     }
 
-    spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, ascending ? band_sel_asc : sel,
+    spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, ascending ? sel_asc : sel,
                                    out + b0 * spmla::kHeads * spmla::kDv,
                                    lse ? lse + b0 * spmla::kHeads : nullptr);
     aa.n_q = bn;

@@ -104,14 +104,25 @@ def test_band_schedule_matches_pages():
     assert g["max_bands"] * g["band"] == g["frontier_printed"]
 
 
+def _up(x, a=256):
+    return -(-x // a) * a
+
+
 def test_workspace_bytes():
-    w = workloads.PREFILL_8192
-    d = desc_of(w)
+    """Scores of one selection group (consecutive bands whose score matrix
+    fits 128 MiB) + that group's selections in two orders."""
+    w = workloads.PREFILL_8192  # 16 MiB of scores per band: all four bands in one group
+    nb = sp.spmla_prefill_workspace_bytes(desc_of(w))
+    assert nb == 8192 * 2048 * 4 + 2 * 8192 * 512 * 4
+    w = workloads.PREFILL_9133  # row stride 2,284; 18.7 MB per band: all five bands fit
+    nb = sp.spmla_prefill_workspace_bytes(desc_of(w))
+    assert nb == _up(9133 * 2284 * 4) + 2 * _up(9133 * 512 * 4)
+    d = sp.make_desc(20480, 0, 128, 512)  # 5,120 rows: 40 MiB per band, 3 bands per group
     nb = sp.spmla_prefill_workspace_bytes(d)
-    assert nb == 2048 * 2048 * 4 + 2 * 2048 * 512 * 4  # scores + selections in two orders
-    w4 = workloads.CHUNK_8192_AT_114687
+    assert nb == 6144 * 5120 * 4 + 2 * 6144 * 512 * 4
+    w4 = workloads.CHUNK_8192_AT_114687  # 240 MiB of scores per band: one band per group
     nb4 = sp.spmla_prefill_workspace_bytes(desc_of(w4))
-    assert nb4 >= 2048 * 30719 * 4 + 2048 * 2048 * 4
+    assert nb4 == 2048 * 30720 * 4 + 2 * 2048 * 2048 * 4
 
 
 def test_workspace_covers_split_partials_and_fused_candidates():
@@ -129,8 +140,8 @@ def test_workspace_covers_split_partials_and_fused_candidates():
     nb = sp.spmla_prefill_workspace_bytes(desc_of(w))
     n_spans = -(-w.n_comp // 512)
     assert nb >= 2048 * n_spans * 128 * 8 + 2048 * n_spans * 4  # candidate slots + counts
-    # a call too large for splits needs no partials: the dense band dominates
-    assert sp.spmla_prefill_workspace_bytes(desc_of(workloads.PREFILL_8192)) == 2048 * 2048 * 4 + 2 * 2048 * 512 * 4
+    # a call too large for splits needs no partials: the group's scores dominate
+    assert sp.spmla_prefill_workspace_bytes(desc_of(workloads.PREFILL_8192)) == 8192 * 2048 * 4 + 2 * 8192 * 512 * 4
 
 
 A = 1 << 20  # an aligned fake address; never dereferenced by these calls

@@ -300,6 +300,52 @@ def test_band_invariant_long_history(sp):
     assert_close(np.array(got), np.array(want), "long-history rows vs oracle")
 
 
+GROUPS = [
+    # a dense selection group of three 1,024-query bands, then a fused band
+    # (its first token sees 4,352 > 4,096 compressed rows); band 512 regroups
+    # six dense bands, band 4,096 is one dense band
+    ("dense-then-fused", workloads.LayerShape("groups-a", n_q=4096, q_pos0=14336, window=128, top_k=512,
+                                              band=1024), (4096, 512), 14),
+    # 84 MB of scores per 4,096-query band: five one-band groups; at band 2,048
+    # the 128 MiB budget makes groups of three bands (6,144 rows) and a rest
+    ("budget-splits-groups", workloads.LayerShape("groups-b", n_q=20480, q_pos0=0, window=128, top_k=512,
+                                                  band=4096), (2048,), 15),
+]
+
+
+@pytest.mark.parametrize("name,w,other_bands,seed", GROUPS, ids=[g[0] for g in GROUPS])
+def test_selection_groups_band_invariant(sp, name, w, other_bands, seed):
+    """spmla_prefill selects the queries of consecutive dense bands with one
+    indexer and one top-k launch (up to a score budget) and attends band by
+    band. Grouping, band size and a missing sel_out must not change a bit;
+    sampled rows at group and band edges match the oracle."""
+    import torch
+
+    say(f"[parity] selection groups, {name}: n_q={w.n_q} q_pos0={w.q_pos0} band={w.band} others={other_bands}")
+    x = workloads.generate(w, seed=seed)
+    dev = to_dev(x)
+    o1, l1, s1 = sp.prefill(desc_of(sp, w), dev)
+    o2, l2, _ = sp.prefill(desc_of(sp, w), dev, want_sel=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "outputs differ without sel_out"
+    del o2, l2
+    for band in other_bands:
+        o3, l3, s3 = sp.prefill(desc_of(sp, w, band=band), dev)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s3), f"sel differs at band {band}"
+        assert torch.equal(o1, o3), f"out differs at band {band}"
+        assert torch.equal(l1, l3), f"lse differs at band {band}"
+        del o3, l3, s3
+    rows = sorted({0, w.band - 1, w.band, 3 * w.band - 1, 3 * w.band, 6143, 6144, w.n_q - 1} & set(range(w.n_q)))
+    got, want = [], []
+    for r in rows:
+        ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k, scale=w.scale,
+                             d_v=w.d_v, q_begin=r, q_end=r + 1)
+        np.testing.assert_array_equal(s1[r].cpu().numpy(), ref["sel"][0], err_msg=f"sel row {r}")
+        got.append(o1[r].cpu().numpy()), want.append(ref["out"][0])
+    assert_close(np.array(got), np.array(want), f"{name} rows {rows} vs oracle")
+
+
 @pytest.mark.parametrize("case", ["short-history", "long-history"])
 def test_optional_outputs_may_be_null(sp, case):
     """spmla_prefill without sel_out (the selection then lives only in the
