@@ -483,7 +483,7 @@ template <int SRC>
 hipError_t launch_by_size(int n, const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
   if (n <= 256 * 4) return launch_cfg<256, 4, SRC>(a, f, grid, stream);
   if (n <= 256 * 8) return launch_cfg<256, 8, SRC>(a, f, grid, stream);
-  if (n <= 512 * 8) return launch_cfg<512, 8, SRC>(a, f, grid, stream);
+  if (n <= 256 * 16) return launch_cfg<256, 16, SRC>(a, f, grid, stream);
   if (n <= 1024 * 8) return launch_cfg<1024, 8, SRC>(a, f, grid, stream);
   if (n <= 1024 * 16) return launch_cfg<1024, 16, SRC>(a, f, grid, stream);
   return launch_cfg<1024, 32, SRC>(a, f, grid, stream);  // n <= 32768 (host-checked)
