@@ -212,13 +212,14 @@ int spmla_compress(const spmla_desc* desc, const uint16_t* kv_raw, uint16_t* kv_
                    void* stream);
 
 /*
- * Workspace bytes spmla_prefill needs for this descriptor: the indexer
- * scores of one selection group (or, when larger, the fused selection's
- * candidate slots for one band or the key-split partials of a small call)
- * plus that group's selected rows twice (score order, and ascending row
- * order for the attention's gathers). A selection group is the largest
- * number of whole bands whose score matrix fits 128 MiB (at least one band;
- * all of them when they fit).
+ * Workspace bytes spmla_prefill needs for this descriptor: the largest
+ * selection scratch of its selection groups (a group's indexer scores, or
+ * its fused handoff's thresholds, slot counts and candidate slots), or the
+ * key-split partials of a small call when larger, plus the selected rows of
+ * its largest group twice (score order, and ascending row order for the
+ * attention's gathers). A selection group is a run of consecutive whole
+ * bands that select the same way, as many as fit 128 MiB of scores or
+ * 512 MiB of fused-handoff scratch (at least one band).
  * Returns SPMLA_OK and writes *bytes, or an error code.
  */
 int spmla_prefill_workspace_bytes(const spmla_desc* desc, size_t* bytes);
@@ -226,12 +227,12 @@ int spmla_prefill_workspace_bytes(const spmla_desc* desc, size_t* bytes);
 /*
  * Steps 1-4 for all n_q queries in bands of `band` queries, all enqueued on
  * `stream` with no host round trip. Attention runs band by band. Selection
- * either takes the score matrix, for a selection group of consecutive bands
- * at once (one indexer and one top-k launch for all of the group's queries,
- * before the group's first attention launch), or, for a band of at least
- * 256 queries that each see more than 4,096 (and at least 8 * top_k)
- * compressed rows, the fused handoff of that band alone, which never writes
- * the score matrix. Same inputs and outputs as the three calls above;
+ * runs once per selection group, before the group's first attention launch:
+ * through the score matrix (one indexer and one top-k launch for all of the
+ * group's queries), or, for bands of at least 256 queries that each see
+ * more than 4,096 (and at least 8 * top_k) compressed rows, through the
+ * fused handoff, which never writes the score matrix. Same inputs and
+ * outputs as the three calls above;
  * sel_out (int32 [n_q][top_k]) and lse may be NULL. When the compressed
  * rows exceed 4 MiB the attention takes each selection in ascending row
  * order, so out and lse can differ from spmla_sparse_attn on sel_out in

@@ -85,45 +85,78 @@ size_t scores_bytes_per_band(const spmla_desc* d) {
   const int64_t rows = d->band < d->n_q ? d->band : d->n_q;
   return (size_t)rows * (size_t)band_ld(d) * sizeof(int32_t);
 }
-size_t sel_bytes_per_band(const spmla_desc* d) {
-  const int64_t rows = d->band < d->n_q ? d->band : d->n_q;
-  return (size_t)rows * (size_t)d->top_k * sizeof(int32_t);
-}
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Selection groups: consecutive bands whose selection takes the score matrix
-// (not the fused handoff) get one indexer launch and one top-k launch for
-// all their queries, as long as the group's scores fit this budget; the
+constexpr size_t kRowBytes = (size_t)spmla::kDqk * 2;  // one fp16 latent row
+constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator die
+
+// Selection groups: consecutive bands that select the same way get one set
+// of selection launches for all their queries, while the group's scratch
+// fits a budget: the score matrix (dense selection, 128 MiB) or the fused
+// handoff's thresholds, slot counts and candidate slots (512 MiB). The
 // attention still runs band by band. One launch per step instead of one per
 // band removes the ramp and tail of short, latency-bound launches.
 constexpr size_t kSelGroupBytes = (size_t)128 << 20;
-int64_t sel_group_rows(const spmla_desc* d) {
+constexpr size_t kFusedGroupBytes = (size_t)512 << 20;
+int64_t group_rows_within(const spmla_desc* d, size_t per_band, size_t budget) {
   const int64_t band_rows = d->band < d->n_q ? d->band : d->n_q;
-  const size_t per_band = scores_bytes_per_band(d);
-  int64_t bands = per_band ? (int64_t)(kSelGroupBytes / per_band) : INT64_MAX / 2 / (band_rows > 0 ? band_rows : 1);
+  int64_t bands = per_band ? (int64_t)(budget / per_band) : INT64_MAX / 2 / (band_rows > 0 ? band_rows : 1);
   if (bands < 1) bands = 1;
   const int64_t rows = bands * band_rows;
   return rows < d->n_q ? rows : d->n_q;
 }
-size_t sel_bytes_per_group(const spmla_desc* d) {
-  return (size_t)sel_group_rows(d) * (size_t)d->top_k * sizeof(int32_t);
+int64_t dense_group_rows(const spmla_desc* d) { return group_rows_within(d, scores_bytes_per_band(d), kSelGroupBytes); }
+int64_t fused_group_rows(const spmla_desc* d) {
+  const int band_rows = d->band < d->n_q ? d->band : d->n_q;
+  const spmla::FusedPlan plan = spmla::fused_plan(d->n_comp, d->top_k);
+  return group_rows_within(d, spmla::fused_workspace_bytes(band_rows, plan), kFusedGroupBytes);
+}
+int band_len(const spmla_desc* d, int64_t b0) { return (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band); }
+bool fused_band(const spmla_desc* d, int64_t b0) {
+  return d->n_comp > 0 && spmla::fused_applies(band_len(d, b0), d->q_pos0 + (int)b0, d->n_comp, d->ratio, d->top_k);
 }
 
-constexpr size_t kRowBytes = (size_t)spmla::kDqk * 2;  // one fp16 latent row
-constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator die
-// Scratch reused by the steps in stream order: the score matrix of a
-// selection group or the fused selection's thresholds, slot counts and
-// candidates (one band), then the attention's key-split partials (small
-// calls only), whichever is largest. A group's scores are dead once its
-// top-k has run, before the first attention launch of the group.
-size_t band_scratch_bytes(const spmla_desc* d) {
-  const int rows = d->band < d->n_q ? d->band : d->n_q;
-  size_t need = round_up((size_t)sel_group_rows(d) * (size_t)band_ld(d) * sizeof(int32_t), 256);
-  const size_t fused = spmla::fused_workspace_bytes(rows, spmla::fused_plan(d->n_comp, d->top_k));
-  const size_t part = round_up(spmla::attn_partial_bytes(rows, spmla::attn_splits(d->n_q)), 256);
-  if (fused > need) need = fused;
-  if (part > need) need = part;
-  return need;
+// Calls f(g0, g1, fused) for the selection groups of a call in order: each
+// is a run of whole bands [g0, g1) that select the same way, as many as fit
+// that way's budget. spmla_prefill runs exactly these groups, and the
+// workspace is sized from them.
+template <typename F>
+void for_each_group(const spmla_desc* d, F&& f) {
+  const int64_t dense_cap = dense_group_rows(d), fused_cap = fused_group_rows(d);
+  for (int64_t g0 = 0; g0 < d->n_q;) {
+    const bool fused = fused_band(d, g0);
+    const int64_t cap = fused ? fused_cap : dense_cap;  // a multiple of the band unless it covers every query
+    int64_t g1 = g0 + band_len(d, g0);
+    while (g1 < d->n_q && g1 - g0 < cap && fused_band(d, g1) == fused) g1 += band_len(d, g1);
+    f(g0, g1, fused);
+    g0 = g1;
+  }
+}
+
+// Workspace layout: scratch reused by the steps in stream order (a group's
+// score matrix or fused-handoff slots, then the attention's key-split
+// partials of a small call; a group's selection scratch is dead once its
+// top-k has run, before its first attention launch), then the selections of
+// the largest group in score order and in ascending row order.
+struct WsLayout {
+  size_t scratch = 0;
+  size_t sel = 0;  // bytes of one selection copy
+  size_t total() const { return scratch + 2 * sel; }
+};
+WsLayout ws_layout(const spmla_desc* d) {
+  WsLayout w;
+  const int band_rows = d->band < d->n_q ? d->band : d->n_q;
+  w.scratch = round_up(spmla::attn_partial_bytes(band_rows, spmla::attn_splits(d->n_q)), 256);
+  int64_t max_rows = 0;
+  for_each_group(d, [&](int64_t g0, int64_t g1, bool fused) {
+    const int64_t rows = g1 - g0;
+    const size_t need = fused ? spmla::fused_workspace_bytes((int)rows, spmla::fused_plan(d->n_comp, d->top_k))
+                              : round_up((size_t)rows * (size_t)band_ld(d) * sizeof(int32_t), 256);
+    if (need > w.scratch) w.scratch = need;
+    if (rows > max_rows) max_rows = rows;
+  });
+  w.sel = round_up((size_t)max_rows * (size_t)d->top_k * sizeof(int32_t), 256);
+  return w;
 }
 
 spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
@@ -267,7 +300,7 @@ int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (!bytes) return fail(SPMLA_EINVAL, "bytes is NULL");
-  *bytes = band_scratch_bytes(d) + 2 * round_up(sel_bytes_per_group(d), 256);
+  *bytes = ws_layout(d).total();
   return ok();
 }
 
@@ -297,105 +330,93 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
 
   hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
-  int32_t* band_scores = reinterpret_cast<int32_t*>(ws);
-  int32_t* band_sel = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d));
+  const WsLayout lay = ws_layout(d);
+  int32_t* scores = reinterpret_cast<int32_t*>(ws);
+  int32_t* ws_sel = reinterpret_cast<int32_t*>(ws + lay.scratch);
+  int32_t* ws_sel_asc = reinterpret_cast<int32_t*>(ws + lay.scratch + lay.sel);
   // Attention takes each selection in ascending row order when the
   // compressed rows outgrow one die's L2: the queries in flight on a die then
   // sweep the rows together and share what they gather (the softmax does not
   // depend on the order of its keys).
   const bool ascending = (size_t)d->n_comp * kRowBytes > kDieL2Bytes;
-  int32_t* band_sel_asc = reinterpret_cast<int32_t*>(ws + band_scratch_bytes(d) + round_up(sel_bytes_per_group(d), 256));
-  const int64_t group_cap = sel_group_rows(d);
-  auto band_len = [&](int64_t b) { return (int)((d->n_q - b) < d->band ? (d->n_q - b) : d->band); };
-  auto fused_band = [&](int64_t b) {
-    return d->n_comp > 0 && spmla::fused_applies(band_len(b), d->q_pos0 + (int)b, d->n_comp, d->ratio, d->top_k);
-  };
 
-  // The current dense selection group covers queries [g0, g1); its
-  // selections start at band_sel / band_sel_asc (or sel_out + g0 * top_k).
-  int64_t g0 = 0, g1 = 0;
-  for (int64_t b0 = 0; b0 < d->n_q; b0 += d->band) {
-    const int bn = band_len(b0);
-    const int pos0 = d->q_pos0 + (int)b0;
-    const bool fused = fused_band(b0);
-    const bool new_group = !fused && b0 >= g1;
-    if (new_group) {
-      // This band and the following ones that also take the score matrix,
-      // up to the group's row budget (whole bands: the budget is a multiple
-      // of the band unless it covers every query).
-      g0 = b0;
-      g1 = b0 + bn;
-      while (g1 < d->n_q && g1 - g0 < group_cap && !fused_band(g1)) g1 += band_len(g1);
-    }
-    const int64_t slot = fused ? 0 : b0 - g0;  // row of this band's selection in the workspace
-    int32_t* sel = sel_out ? sel_out + b0 * d->top_k : band_sel + slot * d->top_k;
-    int32_t* sel_asc = band_sel_asc + slot * d->top_k;
-
+  for_each_group(d, [&](int64_t g0, int64_t g1, bool fused) {
+    if (rc) return;
+    const int gn = (int)(g1 - g0);
+    const int gpos0 = d->q_pos0 + (int)g0;
+    // The group's selections: rows g0 .. g1-1 of sel_out, or the workspace.
+    int32_t* gsel = sel_out ? sel_out + g0 * d->top_k : ws_sel;
     if (fused) {
-      // Long history: indexer -> top-k handoff without the score band.
+      // Long history: indexer -> top-k handoff without the score matrix.
       spmla::FusedArgs fa{};
-      fa.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
-      fa.iw = iw + b0 * spmla::kIdxHeads;
+      fa.iq = iq + g0 * spmla::kIdxHeads * spmla::kIdxDim;
+      fa.iw = iw + g0 * spmla::kIdxHeads;
       fa.ik = ik;
-      fa.sel = sel;
+      fa.sel = gsel;
       fa.n_sel = nullptr;
-      fa.sel_asc = ascending ? sel_asc : nullptr;
-      fa.n_q = bn;
-      fa.q_pos0 = pos0;
+      fa.sel_asc = ascending ? ws_sel_asc : nullptr;
+      fa.n_q = gn;
+      fa.q_pos0 = gpos0;
       fa.n_comp = d->n_comp;
       fa.ratio = d->ratio;
       fa.top_k = d->top_k;
       fa.plan = spmla::fused_plan(d->n_comp, d->top_k);
       spmla::fused_bind_workspace(fa, ws);
       rc = hip_status(spmla::launch_fused_topk(fa, st), "fused selection launch");
-      if (rc) return rc;
-    } else if (new_group) {
-      const int gn = (int)(g1 - g0);
+      if (rc) return;
+    } else {
       if (d->n_comp > 0) {
         spmla::IndexerArgs ia;
-        ia.iq = iq + b0 * spmla::kIdxHeads * spmla::kIdxDim;
-        ia.iw = iw + b0 * spmla::kIdxHeads;
+        ia.iq = iq + g0 * spmla::kIdxHeads * spmla::kIdxDim;
+        ia.iw = iw + g0 * spmla::kIdxHeads;
         ia.ik = ik;
-        ia.scores = band_scores;
+        ia.scores = scores;
         ia.ld_scores = band_ld(d);
         ia.n_q = gn;
-        ia.q_pos0 = pos0;
+        ia.q_pos0 = gpos0;
         ia.n_comp = d->n_comp;
         ia.ratio = d->ratio;
         ia.fill_invisible = 0;  // top-k reads only the rows each token can see
         ia.span = 0;
         rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
-        if (rc) return rc;
+        if (rc) return;
       }
       spmla::TopkArgs ta;
-      ta.scores = band_scores;
+      ta.scores = scores;
       ta.ld_scores = band_ld(d);
-      ta.sel = sel;
+      ta.sel = gsel;
       ta.n_sel = nullptr;
-      ta.sel_asc = ascending ? sel_asc : nullptr;
+      ta.sel_asc = ascending ? ws_sel_asc : nullptr;
       ta.n_q = gn;
-      ta.q_pos0 = pos0;
+      ta.q_pos0 = gpos0;
       ta.n_comp = d->n_comp;
       ta.ratio = d->ratio;
       ta.top_k = d->top_k;
       rc = hip_status(spmla::launch_topk(ta, st), "top-k launch");
-      if (rc) return rc;
+      if (rc) return;
     }
 
-    spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, ascending ? sel_asc : sel,
-                                   out + b0 * spmla::kHeads * spmla::kDv,
-                                   lse ? lse + b0 * spmla::kHeads : nullptr);
-    aa.n_q = bn;
-    aa.q_pos0 = pos0;
-    aa.splits = spmla::attn_splits(d->n_q);
-    if (aa.splits > 1) {  // a small call: split each key list, partials in the band scratch
-      const size_t items = (size_t)bn * aa.splits;
-      aa.part_o = reinterpret_cast<float*>(ws);
-      aa.part_ml = aa.part_o + items * spmla::kHeads * spmla::kDv;
+    // Attention band by band.
+    for (int64_t b0 = g0; b0 < g1; b0 += d->band) {
+      const int bn = band_len(d, b0);
+      const int64_t row = b0 - g0;  // first row of this band's selections within the group
+      const int32_t* sel = ascending ? ws_sel_asc + row * d->top_k : gsel + row * d->top_k;
+      spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
+                                     out + b0 * spmla::kHeads * spmla::kDv,
+                                     lse ? lse + b0 * spmla::kHeads : nullptr);
+      aa.n_q = bn;
+      aa.q_pos0 = d->q_pos0 + (int)b0;
+      aa.splits = spmla::attn_splits(d->n_q);
+      if (aa.splits > 1) {  // a small call: split each key list, partials in the scratch
+        const size_t items = (size_t)bn * aa.splits;
+        aa.part_o = reinterpret_cast<float*>(ws);
+        aa.part_ml = aa.part_o + items * spmla::kHeads * spmla::kDv;
+      }
+      rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
+      if (rc) return;
     }
-    rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
-    if (rc) return rc;
-  }
+  });
+  if (rc) return rc;
   return ok();
 }
 

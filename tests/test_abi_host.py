@@ -120,9 +120,15 @@ def test_workspace_bytes():
     d = sp.make_desc(20480, 0, 128, 512)  # 5,120 rows: 40 MiB per band, 3 bands per group
     nb = sp.spmla_prefill_workspace_bytes(d)
     assert nb == 6144 * 5120 * 4 + 2 * 6144 * 512 * 4
-    w4 = workloads.CHUNK_8192_AT_114687  # 240 MiB of scores per band: one band per group
+    # long history: every band takes the fused handoff, whose thresholds, slot
+    # counts and 60 spans x 128 candidate slots per query (126 MB per band)
+    # fit 512 MiB four bands at a time; that exceeds one band of scores
+    w4 = workloads.CHUNK_8192_AT_114687
     nb4 = sp.spmla_prefill_workspace_bytes(desc_of(w4))
-    assert nb4 == 2048 * 30720 * 4 + 2 * 2048 * 2048 * 4
+    n, spans = 8192, 60
+    fused = _up(n * 4) + _up(4) + _up(n * 4) + _up(n * spans * 4) + _up(n * spans * 128 * 8)
+    assert fused > 2048 * 30720 * 4
+    assert nb4 == fused + 2 * n * 2048 * 4
 
 
 def test_workspace_covers_split_partials_and_fused_candidates():

@@ -310,6 +310,10 @@ GROUPS = [
     # the 128 MiB budget makes groups of three bands (6,144 rows) and a rest
     ("budget-splits-groups", workloads.LayerShape("groups-b", n_q=20480, q_pos0=0, window=128, top_k=512,
                                                   band=4096), (2048,), 15),
+    # long history: three fused bands of 512 queries share one fused selection
+    # group; one band of 1,536 and six fused bands of 256 must agree
+    ("fused-group", workloads.LayerShape("groups-c", n_q=1536, q_pos0=114687, window=128, top_k=2048,
+                                         band=512), (1536, 256), 16),
 ]
 
 
