@@ -869,15 +869,22 @@ void attn_kernel(AttnArgs a) {
 
 // Combines the key splits of one (query, head): with M the largest split
 // reference, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s and
-// lse = (M + log2 of that sum) * ln 2, splits summed in order. The split
-// weights are formed once in LDS; the partial rows are read with independent
-// loads (8 splits in flight per thread).
+// lse = (M + log2 of that sum) * ln 2. A workgroup takes one quarter of the
+// value dims of one (query, head); its four split groups each sum every
+// fourth split (8 loads in flight per thread) and meet in LDS in a fixed
+// order, and the l sum is a fixed shuffle tree, so results do not depend on
+// timing.
 constexpr int kMaxSplits = 64;
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+constexpr int kMergeParts = 4;   // value-dim quarters per (query, head)
+constexpr int kMergeGroups = 4;  // split groups per workgroup
+constexpr int kMergeCols = kDv / kMergeParts / 4;  // float4 columns per quarter
+__global__ __launch_bounds__(kMergeCols * kMergeGroups) void attn_merge_kernel(AttnArgs a) {
   __shared__ float w_s[kMaxSplits];
   __shared__ float s_lsum, s_mmax;
-  const int r = blockIdx.x / kHeads;
-  const int h = blockIdx.x % kHeads;
+  __shared__ float4v part[kMergeGroups - 1][kMergeCols];
+  const int qd = blockIdx.x % kMergeParts;
+  const int h = (blockIdx.x / kMergeParts) % kHeads;
+  const int r = blockIdx.x / (kMergeParts * kHeads);
   const int tid = threadIdx.x;
   const int ns = a.splits;  // <= kMaxSplits
   if (tid < 64) {
@@ -890,32 +897,39 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
     for (int o = 32; o > 0; o >>= 1) m_max = fmaxf(m_max, __shfl_xor(m_max, o));
     const float w = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - m_max);
     if (has) w_s[tid] = w;
-    // l sum in split order (a fixed order for every launch)
     float wl = w * l;
-    float total = 0.f;
-    for (int s = 0; s < ns; ++s) total += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wl += __shfl_xor(wl, o);
     if (tid == 0) {
-      s_lsum = total;
+      s_lsum = wl;
       s_mmax = m_max;
     }
   }
   __syncthreads();
-  const int d = 4 * tid;
+  const int col = tid % kMergeCols;
+  const int sg = tid / kMergeCols;
+  const int d = qd * (kDv / kMergeParts) + 4 * col;
   const float* po = a.part_o + ((int64_t)r * ns * kHeads + h) * kDv + d;
   const int64_t stride = (int64_t)kHeads * kDv;
   float4v o = float4v{0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
+  int s = sg;
+  for (; s + 7 * kMergeGroups < ns; s += 8 * kMergeGroups) {
     float4v p[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const float4v*>(po + (s + u) * stride);
+    for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const float4v*>(po + (s + u * kMergeGroups) * stride);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o += w_s[s + u] * p[u];
+    for (int u = 0; u < 8; ++u) o += w_s[s + u * kMergeGroups] * p[u];
   }
-  for (; s < ns; ++s) o += w_s[s] * *reinterpret_cast<const float4v*>(po + s * stride);
+  for (; s < ns; s += kMergeGroups) o += w_s[s] * *reinterpret_cast<const float4v*>(po + s * stride);
+  if (sg > 0) part[sg - 1][col] = o;
+  __syncthreads();
+  if (sg != 0) return;
+#pragma unroll
+  for (int g = 0; g < kMergeGroups - 1; ++g) o += part[g][col];
   const float l_sum = s_lsum;
   *reinterpret_cast<float4v*>(a.out + ((int64_t)r * kHeads + h) * kDv + d) = o * (1.0f / l_sum);
-  if (a.lse && tid == 0) a.lse[(int64_t)r * kHeads + h] = (s_mmax + __builtin_amdgcn_logf(l_sum)) * 0.69314718055994531f;
+  if (a.lse && qd == 0 && tid == 0)
+    a.lse[(int64_t)r * kHeads + h] = (s_mmax + __builtin_amdgcn_logf(l_sum)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -942,7 +956,8 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
                      dim3(grid), dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_q * kHeads), dim3(kDv / 4), 0, stream, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_q * kHeads * kMergeParts), dim3(kMergeCols * kMergeGroups), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
