@@ -143,7 +143,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   __shared__ int aux[BLOCK + 1];  // span offsets (candidates) or the query row (recompute)
   // Candidates: the span of each collected slot (spans < 256).
   __shared__ unsigned char span_of[SRC == kCandidate ? BLOCK * PER : 1];
-  static_assert(SRC != kCandidate || BLOCK <= 256, "span indices fit a byte");
+  static_assert(SRC != kCandidate || (kMaxComp + 511) / 512 <= 255, "span indices fit a byte");
   extern __shared__ u64 keys[];
 
   const int tid = threadIdx.x;
@@ -489,8 +489,8 @@ hipError_t launch_by_size(int n, const TopkArgs& a, const FusedArgs& f, int grid
   return launch_cfg<1024, 32, SRC>(a, f, grid, stream);  // n <= 32768 (host-checked)
 }
 
-constexpr int kFinishBlock = 256;
-constexpr int kFinishPer = 16;  // candidates a finish workgroup holds: 4096
+constexpr int kFinishBlock = 512;
+constexpr int kFinishPer = 8;  // candidates a finish workgroup holds: 4096
 constexpr int kRedoGrid = 128;  // workgroups that share the recompute list
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
