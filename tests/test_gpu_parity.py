@@ -151,6 +151,33 @@ def test_full_size_prefill_sampled(sp, name):
     assert_close(np.array(got_lse), np.array(want_lse), f"{name} lse[sampled]")
 
 
+def test_prefill_8192_whole_tensor(sp):
+    """The benchmarked workload in the benchmarked launch configuration,
+    compared whole: every selected index of all 8,192 queries bit-exact, and
+    out and lse within max-abs 2e-3 and NMSE 1e-6 over the entire tensors (the
+    oracle computes the whole layer in about 10 s on 16 host cores)."""
+    import time
+
+    import torch
+
+    w = workloads.PREFILL_8192
+    say(f"[parity whole] {w.name}: generating")
+    x = workloads.generate(w)
+    dev = to_dev(x)
+    say(f"[parity whole] {w.name}: running spmla_prefill")
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    del dev
+    t0 = time.perf_counter()
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    say(f"[parity whole] {w.name}: oracle {time.perf_counter() - t0:.1f} s")
+    np.testing.assert_array_equal(sel, ref["sel"])
+    assert_close(out, ref["out"], f"{w.name} out[all]")
+    assert_close(lse, ref["lse"], f"{w.name} lse[all]")
+
+
 @pytest.mark.parametrize("name", ["decode-1-at-122878", "verify-5-at-122874"])
 def test_decode_and_verify_lanes(sp, name):
     """1 and 5 query lanes after 122,874+ tokens: every lane against the
