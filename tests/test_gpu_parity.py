@@ -151,16 +151,18 @@ def test_full_size_prefill_sampled(sp, name):
     assert_close(np.array(got_lse), np.array(want_lse), f"{name} lse[sampled]")
 
 
-def test_prefill_8192_whole_tensor(sp):
-    """The benchmarked workload in the benchmarked launch configuration,
-    compared whole: every selected index of all 8,192 queries bit-exact, and
-    out and lse within max-abs 2e-3 and NMSE 1e-6 over the entire tensors (the
-    oracle computes the whole layer in about 10 s on 16 host cores)."""
+@pytest.mark.parametrize("name", ["prefill-8192", "prefill-9133"])
+def test_prefill_whole_tensor(sp, name):
+    """The benchmarked workload (and the 9,133-token one, five bands with a
+    ragged last) in the benchmarked launch configuration, compared whole:
+    every selected index of every query bit-exact, and out and lse within
+    max-abs 2e-3 and NMSE 1e-6 over the entire tensors (the oracle computes
+    a whole layer in about 10 s on 16 host cores)."""
     import time
 
     import torch
 
-    w = workloads.PREFILL_8192
+    w = workloads.BY_NAME[name]
     say(f"[parity whole] {w.name}: generating")
     x = workloads.generate(w)
     dev = to_dev(x)
