@@ -935,7 +935,7 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void attn_merge_kernel(A
 }  // namespace
 
 int attn_splits(int n_q_call) {
-  if (n_q_call >= 512) return 1;
+  if (n_q_call >= 512 || n_q_call <= 0) return 1;  // an empty call has nothing to split
   const int s = (1024 + n_q_call - 1) / n_q_call;
   return s < kMaxSplits ? s : kMaxSplits;
 }

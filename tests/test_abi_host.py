@@ -150,6 +150,18 @@ def test_workspace_covers_split_partials_and_fused_candidates():
     assert sp.spmla_prefill_workspace_bytes(desc_of(workloads.PREFILL_8192)) == 8192 * 2048 * 4 + 2 * 8192 * 512 * 4
 
 
+def test_empty_call():
+    """No queries: the workspace is empty and spmla_prefill returns at once,
+    before any pointer is looked at."""
+    lib = sp.load_library()
+    d = sp.make_desc(0, 100, 128, 512)
+    assert sp.spmla_check_desc(d) == 0
+    assert sp.spmla_prefill_workspace_bytes(d) == 0
+    assert sp.spmla_num_bands(d) == 0
+    ptrs = [0] * 10
+    assert lib.spmla_prefill(ctypes.byref(d), *[ctypes.c_void_p(p) for p in ptrs], ctypes.c_size_t(0), None) == sp.SPMLA_OK
+
+
 A = 1 << 20  # an aligned fake address; never dereferenced by these calls
 
 
