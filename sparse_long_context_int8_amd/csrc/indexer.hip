@@ -186,8 +186,10 @@ __device__ __forceinline__ int code_lo(int c) {
 constexpr int kCodes = 2048;
 
 // Threshold pass (also clears the recompute list of the finish pass): one
-// workgroup per 4 tokens (one A tile); its 4 waves take
-// turns over 16-row steps of the sampled rows j = stride * i. Each sampled
+// workgroup per 4 tokens (one A tile); its 4 waves take turns over the
+// sampled rows, one block of 16 consecutive rows in every 16 * stride (whole
+// 128-byte lines of the int8 keys, where single rows every stride apart would
+// use half of each line). Each sampled
 // visible score lands in a per-token LDS histogram of score codes; the
 // threshold is the lowest score of the code bin in which the count from the
 // top reaches `rank` (INT32_MIN if fewer samples than that).
@@ -218,14 +220,14 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
     v4i b[kUnroll];
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
-      const int j = stride * (16 * (s0 + q) + col);
+      const int j = 16 * stride * (s0 + q) + col;
       b[q] = (s0 + q < n_steps && j < a.n_comp)
                  ? *reinterpret_cast<const v4i*>(a.ik + (int64_t)j * kIdxDim + grp * 16)
                  : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
-      const int j = stride * (16 * (s0 + q) + col);
+      const int j = 16 * stride * (s0 + q) + col;
       const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, b[q], v4i{0, 0, 0, 0}, 0, 0, 0);
       if (s0 + q < n_steps && j < nv) atomicAdd(&hist[grp][score_code(head_sum(acc, hw))], 1);
     }

@@ -505,7 +505,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
 // The fused selection serves a launch of at least 256 tokens (fewer leave
 // its passes latency-bound, and their score band is small) when every token
 // keeps at most 2048 of more than 4096 visible rows and sees at least 8 rows
-// per kept row, so that the 1-in-8 sample holds enough rows above the
+// per kept row, so that the 1-in-8 sample (16-row blocks) holds enough rows above the
 // threshold.
 bool fused_applies(int n_q, int q_pos0, int n_comp, int ratio, int top_k) {
   if (n_q < 256 || top_k > 2048) return false;

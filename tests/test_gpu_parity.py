@@ -493,9 +493,10 @@ def test_random_shapes(sp, w):
 def test_fused_selection_recompute_paths(sp, case):
     """Long history (256 tokens, each sees ~30K rows and keeps 2,048): the sampled
     threshold is wrong on purpose for some tokens, through overflowing
-    candidate slots (all scores tie at 0) or through a 1-in-8 sample that sees
-    twice the true share of high rows, so those tokens must be redone from
-    recomputed scores; indices stay bit-exact either way."""
+    candidate slots (all scores tie at 0) or through a sample (one block of 16
+    rows in every 128) that finds half of its rows high while one row in 16
+    is, so fewer than 2,048 rows pass the threshold and those tokens must be
+    redone from recomputed scores; indices stay bit-exact either way."""
     w = workloads.LayerShape("fused", n_q=256, q_pos0=120000, window=16, top_k=2048)
     say(f"[parity fused] {case}")
     x = workloads.generate(w, seed=11)
@@ -503,7 +504,7 @@ def test_fused_selection_recompute_paths(sp, case):
         x["iq"][0::2] = 0
     else:
         ik = np.full_like(x["ik"], -8)
-        ik[0::16] = 7
+        ik[(np.arange(len(ik)) % 128) < 8] = 7  # rows 0-7 of every 128: inside the sampled blocks
         x["ik"] = ik
         x["iq"][:] = 7
     dev = to_dev(x)
