@@ -238,16 +238,28 @@ def spmla_prefill(desc, q, kv_comp, kv_raw, iq, iw, ik, out, lse, sel_out, works
 def prefill(desc, dev: dict, want_sel=True, want_lse=True, stream=None):
     """Allocate outputs and workspace with torch and run spmla_prefill.
 
-    `dev` holds device tensors q, kv_comp, kv_raw, iq, iw, ik.
+    `dev` holds device tensors q, kv_comp, kv_raw, iq, iw, ik. With a
+    `stream` (a torch stream or a raw hipStream_t), outputs and workspace are
+    allocated on that stream, so torch's allocator reuses the workspace only
+    in that stream's order once this function drops it; the caller orders
+    the inputs before the call and synchronizes before reading the outputs.
     Returns (out, lse or None, sel or None).
     """
+    import contextlib
+
     torch = _dt()
     device = dev["q"].device
-    out = torch.empty((desc.n_q, desc.n_heads, desc.d_v), dtype=torch.float32, device=device)
-    lse = torch.empty((desc.n_q, desc.n_heads), dtype=torch.float32, device=device) if want_lse else None
-    sel = torch.empty((desc.n_q, desc.top_k), dtype=torch.int32, device=device) if want_sel else None
-    nbytes = spmla_prefill_workspace_bytes(desc)
-    ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
-    spmla_prefill(desc, dev["q"], dev["kv_comp"], dev["kv_raw"], dev["iq"], dev["iw"], dev["ik"],
-                  out, lse, sel, ws, nbytes, stream)
+    if stream is None:
+        ctx = contextlib.nullcontext()
+    else:
+        ts = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+        ctx = torch.cuda.stream(ts)
+    with ctx:
+        out = torch.empty((desc.n_q, desc.n_heads, desc.d_v), dtype=torch.float32, device=device)
+        lse = torch.empty((desc.n_q, desc.n_heads), dtype=torch.float32, device=device) if want_lse else None
+        sel = torch.empty((desc.n_q, desc.top_k), dtype=torch.int32, device=device) if want_sel else None
+        nbytes = spmla_prefill_workspace_bytes(desc)
+        ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
+        spmla_prefill(desc, dev["q"], dev["kv_comp"], dev["kv_raw"], dev["iq"], dev["iw"], dev["ik"],
+                      out, lse, sel, ws, nbytes, stream)
     return out, lse, sel

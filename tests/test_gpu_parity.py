@@ -408,6 +408,39 @@ def test_optional_outputs_may_be_null(sp, case):
     assert_close(o2[r].cpu().numpy(), ref["out"][0], f"{w.name} last row vs oracle")
 
 
+def test_calls_on_side_streams_run_concurrently(sp):
+    """Every call only enqueues on the caller's stream and the library keeps
+    no state between calls: two different prefills (dense selection groups,
+    and long-history fused bands), each with its own workspace, run at the
+    same time on two side streams and give bit-identical results to the same
+    calls on the default stream."""
+    import torch
+
+    shapes = [
+        (workloads.LayerShape("streams-dense", n_q=700, q_pos0=3000, window=128, top_k=512, band=300), 17),
+        (workloads.LayerShape("streams-fused", n_q=512, q_pos0=114687, window=128, top_k=2048, band=256), 18),
+    ]
+    say("[parity streams] two calls on two side streams")
+    runs = []
+    for w, seed in shapes:
+        x = workloads.generate(w, seed=seed)
+        dev = to_dev(x)
+        ref = sp.prefill(desc_of(sp, w), dev)
+        runs.append((w, dev, ref))
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    got = []
+    for (w, dev, _), st in zip(runs, side):
+        st.wait_stream(main)  # inputs were written on the default stream
+        got.append(sp.prefill(desc_of(sp, w), dev, stream=st))
+    for st in side:
+        st.synchronize()
+    for (w, _, ref), res in zip(runs, got):
+        for a_, b_, what in zip(ref, res, ("out", "lse", "sel")):
+            assert torch.equal(a_, b_), f"{w.name}: {what} differs on a side stream"
+
+
 def test_first_query_is_its_own_row(sp):
     """Query 0 sees one key (its own raw row): softmax weight exactly 1."""
     import torch
