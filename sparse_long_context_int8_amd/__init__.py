@@ -136,19 +136,64 @@ def _check(rc: int) -> int:
     return rc
 
 
-def _ptr(t, dtype=None, name="tensor"):
-    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+def _validate(t, dtype=None, name="tensor", numel=0):
+    """dtype, layout and element count of one argument. The library sees
+    only pointers, so the count is checked here against `numel`, the count
+    the descriptor implies: a short tensor raises instead of reaching a
+    kernel."""
+    if t is None or isinstance(t, int):
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the descriptor needs {numel}")
+
+
+def _ptr(t, dtype=None, name="tensor", numel=0):
+    """Device pointer of a contiguous device tensor (None -> NULL; an int is
+    a raw address, used by tests of the C checks)."""
+    _validate(t, dtype, name, numel)
     if t is None:
         return None
-    if isinstance(t, int):  # raw address, used by tests of the C checks
+    if isinstance(t, int):
         return ctypes.c_void_p(t)
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptrs(*specs):
+    """Pointers of several arguments, each (tensor, dtype, name, numel):
+    every argument is validated before any is looked up on the device."""
+    for spec in specs:
+        _validate(*spec)
+    return [_ptr(*spec) for spec in specs]
+
+
+def _n(desc, name: str) -> int:
+    """Element count of an argument as include/spmla.h lays it out."""
+    n_q, n_comp = desc.n_q, desc.n_comp
+    return {
+        "q": n_q * desc.n_heads * desc.d_qk,
+        "kv_comp": n_comp * desc.d_qk,
+        "kv_raw": desc.n_raw * desc.d_qk,
+        "iq": n_q * desc.idx_heads * desc.idx_dim,
+        "iw": n_q * desc.idx_heads,
+        "ik": n_comp * desc.idx_dim,
+        "scores": n_q * n_comp,
+        "sel": n_q * desc.top_k,
+        "out": n_q * desc.n_heads * desc.d_v,
+        "lse": n_q * desc.n_heads,
+    }[name]
+
+
+def _attn_ptrs(desc, q, kv_comp, kv_raw, sel, out, lse):
+    torch = _dt()
+    return _ptrs((q, torch.float16, "q", _n(desc, "q")), (kv_comp, torch.float16, "kv_comp", _n(desc, "kv_comp")),
+                 (kv_raw, torch.float16, "kv_raw", _n(desc, "kv_raw")), (sel, torch.int32, "sel", _n(desc, "sel")),
+                 (out, torch.float32, "out", _n(desc, "out")), (lse, torch.float32, "lse", _n(desc, "lse")))
 
 
 def _stream(stream):
@@ -182,37 +227,37 @@ def spmla_num_bands(desc: spmla_desc) -> int:
 def spmla_indexer_scores(desc, iq, iw, ik, scores, stream=None) -> None:
     torch = _dt()
     _check(load_library().spmla_indexer_scores(
-        ctypes.byref(desc), _ptr(iq, torch.int8, "iq"), _ptr(iw, torch.int8, "iw"),
-        _ptr(ik, torch.int8, "ik"), _ptr(scores, torch.int32, "scores"), _stream(stream)))
+        ctypes.byref(desc), *_ptrs((iq, torch.int8, "iq", _n(desc, "iq")), (iw, torch.int8, "iw", _n(desc, "iw")),
+                                   (ik, torch.int8, "ik", _n(desc, "ik")),
+                                   (scores, torch.int32, "scores", _n(desc, "scores"))),
+        _stream(stream)))
 
 
 def spmla_topk(desc, scores, sel, n_sel=None, stream=None) -> None:
     torch = _dt()
     _check(load_library().spmla_topk(
-        ctypes.byref(desc), _ptr(scores, torch.int32, "scores"), _ptr(sel, torch.int32, "sel"),
-        _ptr(n_sel, torch.int32, "n_sel"), _stream(stream)))
+        ctypes.byref(desc), *_ptrs((scores, torch.int32, "scores", _n(desc, "scores")),
+                                   (sel, torch.int32, "sel", _n(desc, "sel")), (n_sel, torch.int32, "n_sel", desc.n_q)),
+        _stream(stream)))
 
 
 def spmla_sparse_attn(desc, q, kv_comp, kv_raw, sel, out, lse=None, stream=None) -> None:
     torch = _dt()
     _check(load_library().spmla_sparse_attn(
-        ctypes.byref(desc), _ptr(q, torch.float16, "q"), _ptr(kv_comp, torch.float16, "kv_comp"),
-        _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(sel, torch.int32, "sel"),
-        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+        ctypes.byref(desc), *_attn_ptrs(desc, q, kv_comp, kv_raw, sel, out, lse), _stream(stream)))
 
 
 def spmla_sparse_attn_grouped(desc, q, kv_comp, kv_raw, sel, out, lse=None, stream=None) -> None:
     torch = _dt()
     _check(load_library().spmla_sparse_attn_grouped(
-        ctypes.byref(desc), _ptr(q, torch.float16, "q"), _ptr(kv_comp, torch.float16, "kv_comp"),
-        _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(sel, torch.int32, "sel"),
-        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream)))
+        ctypes.byref(desc), *_attn_ptrs(desc, q, kv_comp, kv_raw, sel, out, lse), _stream(stream)))
 
 
 def spmla_compress(desc, kv_raw, kv_comp, comp_begin=0, stream=None) -> None:
     torch = _dt()
     _check(load_library().spmla_compress(
-        ctypes.byref(desc), _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(kv_comp, torch.float16, "kv_comp"),
+        ctypes.byref(desc), *_ptrs((kv_raw, torch.float16, "kv_raw", _n(desc, "kv_raw")),
+                                   (kv_comp, torch.float16, "kv_comp", _n(desc, "kv_comp"))),
         ctypes.c_int32(comp_begin), _stream(stream)))
 
 
@@ -225,14 +270,19 @@ def spmla_prefill_workspace_bytes(desc) -> int:
 def spmla_prefill(desc, q, kv_comp, kv_raw, iq, iw, ik, out, lse, sel_out, workspace,
                   workspace_bytes=None, stream=None) -> None:
     torch = _dt()
+    held = 0 if workspace is None or isinstance(workspace, int) else workspace.numel() * workspace.element_size()
     if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace_bytes = held
+    elif not isinstance(workspace, int) and workspace is not None and workspace_bytes > held:
+        raise ValueError(f"workspace_bytes={workspace_bytes} exceeds the workspace tensor's {held} bytes")
     _check(load_library().spmla_prefill(
-        ctypes.byref(desc), _ptr(q, torch.float16, "q"), _ptr(kv_comp, torch.float16, "kv_comp"),
-        _ptr(kv_raw, torch.float16, "kv_raw"), _ptr(iq, torch.int8, "iq"),
-        _ptr(iw, torch.int8, "iw"), _ptr(ik, torch.int8, "ik"), _ptr(out, torch.float32, "out"),
-        _ptr(lse, torch.float32, "lse"), _ptr(sel_out, torch.int32, "sel_out"),
-        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace_bytes), _stream(stream)))
+        ctypes.byref(desc),
+        *_ptrs((q, torch.float16, "q", _n(desc, "q")), (kv_comp, torch.float16, "kv_comp", _n(desc, "kv_comp")),
+               (kv_raw, torch.float16, "kv_raw", _n(desc, "kv_raw")), (iq, torch.int8, "iq", _n(desc, "iq")),
+               (iw, torch.int8, "iw", _n(desc, "iw")), (ik, torch.int8, "ik", _n(desc, "ik")),
+               (out, torch.float32, "out", _n(desc, "out")), (lse, torch.float32, "lse", _n(desc, "lse")),
+               (sel_out, torch.int32, "sel_out", _n(desc, "sel")), (workspace, None, "workspace", 0)),
+        ctypes.c_size_t(workspace_bytes), _stream(stream)))
 
 
 def prefill(desc, dev: dict, want_sel=True, want_lse=True, stream=None):

@@ -224,3 +224,56 @@ def test_generator_shapes_and_ranges():
     y = workloads.generate(w)
     for k in x:
         assert (x[k] == y[k]).all()  # seeded
+
+
+def _host_args(w):
+    import torch
+
+    d = desc_of(w)
+    x = workloads.generate(w)
+    t = {k: torch.from_numpy(v) for k, v in x.items()}
+    t["out"] = torch.empty((w.n_q, 16, 512), dtype=torch.float32)
+    t["lse"] = torch.empty((w.n_q, 16), dtype=torch.float32)
+    t["sel"] = torch.empty((w.n_q, w.top_k), dtype=torch.int32)
+    return d, t
+
+
+def test_binding_checks_tensor_sizes_against_the_descriptor():
+    """The library sees only pointers; the binding refuses a tensor shorter
+    than the descriptor implies (and a wrong dtype) before any call, and
+    only then asks for device memory."""
+    import torch
+
+    d, t = _host_args(workloads.TINY_256)
+    args = [t["q"], t["kv_comp"], t["kv_raw"], t["sel"], t["out"], t["lse"]]
+    with pytest.raises(ValueError, match="device tensor"):
+        sp.spmla_sparse_attn(d, *args)
+    for i, name in enumerate(["q", "kv_comp", "kv_raw", "sel", "out", "lse"]):
+        short = list(args)
+        short[i] = args[i].reshape(-1)[:-1]
+        with pytest.raises(ValueError, match=f"{name} holds .* needs {args[i].numel()}"):
+            sp.spmla_sparse_attn(d, *short)
+        with pytest.raises(ValueError, match=f"{name} holds"):
+            sp.spmla_sparse_attn_grouped(d, *short)
+    with pytest.raises(ValueError, match="dtype"):
+        sp.spmla_sparse_attn(d, t["q"].float(), *args[1:])
+    with pytest.raises(ValueError, match="iq holds"):
+        sp.spmla_indexer_scores(d, t["iq"][:-1], t["iw"], t["ik"], None)
+    scores = torch.empty((d.n_q, d.n_comp - 1), dtype=torch.int32)
+    with pytest.raises(ValueError, match="scores holds"):
+        sp.spmla_indexer_scores(d, t["iq"], t["iw"], t["ik"], scores)
+    with pytest.raises(ValueError, match="scores holds"):
+        sp.spmla_topk(d, scores, t["sel"])
+    with pytest.raises(ValueError, match="n_sel holds"):
+        sp.spmla_topk(d, torch.empty((d.n_q, d.n_comp), dtype=torch.int32), t["sel"],
+                      torch.empty((d.n_q - 1,), dtype=torch.int32))
+    with pytest.raises(ValueError, match="kv_comp holds"):
+        sp.spmla_compress(d, t["kv_raw"], t["kv_comp"][:-1])
+    ws = torch.empty((64,), dtype=torch.uint8)
+    pre = [t["q"], t["kv_comp"], t["kv_raw"], t["iq"], t["iw"], t["ik"], t["out"], t["lse"], t["sel"]]
+    with pytest.raises(ValueError, match="exceeds the workspace"):
+        sp.spmla_prefill(d, *pre, ws, 65)
+    with pytest.raises(ValueError, match="ik holds"):
+        sp.spmla_prefill(d, *pre[:5], t["ik"][:-1], *pre[6:], ws)
+    with pytest.raises(ValueError, match="device tensor"):
+        sp.spmla_prefill(d, *pre, ws)
