@@ -24,20 +24,17 @@ namespace spmla {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef short v2s __attribute__((ext_vector_type(2)));
 
-// The weights of one token as two int16 pairs (heads 0,1 and 2,3) for the
-// packed head sum below.
+// The weights of one token, sign-extended.
 struct HeadWeights {
-  v2s w01, w23;
+  int w[4];
 };
 __device__ __forceinline__ HeadWeights head_weights(int wpack) {
   HeadWeights w;
-  w.w01 = v2s{(short)(int8_t)(wpack & 0xff), (short)(int8_t)((wpack >> 8) & 0xff)};
-  w.w23 = v2s{(short)(int8_t)((wpack >> 16) & 0xff), (short)(int8_t)((wpack >> 24) & 0xff)};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) w.w[h] = (int)(int8_t)((wpack >> (8 * h)) & 0xff);
   return w;
 }
-
 constexpr int kQTile = 64;  // query tokens per workgroup (16 per wave)
 constexpr int kJStep = 64;  // compressed rows per step (4 MFMA column tiles)
 
@@ -76,17 +73,16 @@ __device__ __forceinline__ void load_b(const int8_t* ik, int n_comp, int j0, int
 }
 
 // Weighted head sum of one 16x16 result: the 4 heads of the lane's token.
-// Each head dot product is at most 64 * 64 = 4096 in magnitude, so it packs
-// exactly into int16; ReLU and the weighted sum then run as two packed
-// maxima and two int16 dot products with int32 accumulation (exact).
+// A head dot product of 64 int8 pairs is at most 64 * 128 * 128 = 2^20 in
+// magnitude and a weight at most 128, so ReLU'd products and weights both
+// fit the signed 24-bit operands of the full-rate integer multiply-add, and
+// every product (<= 2^27) and the sum (<= 2^29) are exact in int32.
 __device__ __forceinline__ int head_sum(v4i acc, const HeadWeights& w) {
-  v2s p01 = __builtin_bit_cast(v2s, __builtin_amdgcn_perm((unsigned)acc[1], (unsigned)acc[0], 0x05040100u));
-  v2s p23 = __builtin_bit_cast(v2s, __builtin_amdgcn_perm((unsigned)acc[3], (unsigned)acc[2], 0x05040100u));
-  p01 = __builtin_elementwise_max(p01, v2s{0, 0});
-  p23 = __builtin_elementwise_max(p23, v2s{0, 0});
-  return __builtin_amdgcn_sdot2(p23, w.w23, __builtin_amdgcn_sdot2(p01, w.w01, 0, false), false);
+  int s = __mul24(max(acc[0], 0), w.w[0]);
+#pragma unroll
+  for (int h = 1; h < 4; ++h) s += __mul24(max(acc[h], 0), w.w[h]);
+  return s;
 }
-
 // Scores of the lane's token in tile m for rows j0+4c .. j0+4c+3.
 __device__ __forceinline__ v4i tile_scores(const TokenTiles& tt, int m, const v4i (&b)[4]) {
   v4i s;

@@ -115,6 +115,20 @@ def pin_indexer_brute_force(orc):
         want = _indexer_brute(inp["iq"], inp["iw"], inp["ik"], q_pos0, ratio)
         assert got.dtype == np.int32
         np.testing.assert_array_equal(got.astype(np.int64), want)
+    # the whole int8 range, negative weights and the extreme dot products
+    # (+-64*128*128 = +-2^20 per head, weighted sums up to 2^29) stay exact
+    inp = _tiny_inputs(rng, n_q=8, q_pos0=40, ratio=4, H=1, D=4, Hi=4, Di=64, value_range=128)
+    inp["iw"] = rng.integers(-128, 128, inp["iw"].shape).astype(np.int8)
+    inp["iq"][0] = -128
+    inp["ik"][0] = -128
+    inp["iw"][0] = -128
+    inp["iw"][1] = 127
+    inp["iq"][1] = 127
+    inp["ik"][1] = -128
+    got = orc.indexer_scores(inp["iq"], inp["iw"], inp["ik"], 40, 4)
+    want = _indexer_brute(inp["iq"], inp["iw"], inp["ik"], 40, 4)
+    assert want[0, 0] == -128 * 4 * 64 * 128 * 128
+    np.testing.assert_array_equal(got.astype(np.int64), want)
 
 
 def pin_indexer_closed_forms(orc):

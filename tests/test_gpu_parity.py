@@ -552,6 +552,43 @@ def test_fused_selection_recompute_paths(sp, case):
     assert_close(lse.cpu().numpy(), ref["lse"], f"fused {case} lse")
 
 
+FULL_RANGE = [
+    ("dense", workloads.LayerShape("int8-dense", n_q=300, q_pos0=2000, window=32, top_k=128), 31),
+    ("fused", workloads.LayerShape("int8-fused", n_q=256, q_pos0=20000, window=16, top_k=512), 32),
+]
+
+
+@pytest.mark.parametrize("name,w,seed", FULL_RANGE, ids=[f[0] for f in FULL_RANGE])
+def test_indexer_full_int8_range(sp, name, w, seed):
+    """Indexer inputs over the whole int8 range with negative weights: head
+    dot products reach +-2^20 and weighted sums +-2^29, beyond what 16-bit
+    intermediates hold. Scores and selections stay bit-exact, through the
+    score matrix (short history) and the fused handoff (long history)."""
+    import torch
+
+    say(f"[parity int8 range] {name}")
+    x = workloads.generate(w, seed=seed)
+    rng = np.random.default_rng(seed)
+    x["iq"] = rng.integers(-128, 128, x["iq"].shape).astype(np.int8)
+    x["ik"] = rng.integers(-128, 128, x["ik"].shape).astype(np.int8)
+    x["iw"] = rng.integers(-128, 128, x["iw"].shape).astype(np.int8)
+    x["iq"][:4] = -128
+    x["ik"][::7] = -128
+    x["iw"][:2] = -128
+    x["iw"][2:4] = 127
+    dev = to_dev(x)
+    want_sc = oracle.indexer_scores(x["iq"], x["iw"], x["ik"], w.q_pos0, w.ratio)
+    assert np.abs(want_sc.astype(np.int64)).max() >= 2**28
+    want_sel, _ = oracle.topk_select(want_sc, w.q_pos0, w.ratio, w.top_k, w.n_comp)
+    d = desc_of(sp, w)
+    scores = torch.empty((w.n_q, w.n_comp), dtype=torch.int32, device="cuda")
+    sp.spmla_indexer_scores(d, dev["iq"], dev["iw"], dev["ik"], scores)
+    _, _, sel = sp.prefill(d, dev, want_lse=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scores.cpu().numpy(), want_sc)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
+
+
 def test_topk_heavy_ties(sp):
     """Scores from a handful of values: the index tie-break decides most rows."""
     import torch
