@@ -125,6 +125,10 @@ int spmla_num_bands(const spmla_desc* desc);
  *   ik      int8  [n_comp][idx_dim]             (may be NULL if n_comp == 0)
  *   scores  int32 [n_q][n_comp]  (output; exact integers)
  *
+ * Exact for every int8 input: a head dot product is at most 64*128*128 =
+ * 2^20 in magnitude and a score at most 4*128*2^20 = 2^29, so no real
+ * score equals INT32_MIN.
+ *
  * Writes the full n_q x n_comp matrix: meant for tests and short calls;
  * spmla_prefill holds at most 128 MiB of it (one selection group) at once.
  */
