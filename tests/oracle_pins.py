@@ -396,6 +396,64 @@ def pin_band_independence(orc):
         np.testing.assert_array_equal(full[key], np.concatenate([p[key] for p in parts]))
 
 
+def _prefill_brute(inp, q_pos0, ratio, window, top_k, scale, d_v):
+    """One whole layer from the definitions, in plain Python loops: visible
+    compressed rows from their raw members, integer indexer scores, a
+    sorted() top-k, and a math.exp softmax over the selected compressed rows
+    followed by the window's raw rows. Returns (sel, out, lse) lists."""
+    q, kv_comp, kv_raw = inp["q"], inp["kv_comp"], inp["kv_raw"]
+    iq, iw, ik = inp["iq"], inp["iw"], inp["ik"]
+    T, H, D = q.shape
+    Hi, Di = iq.shape[1], iq.shape[2]
+    sels, outs, lses = [], [], []
+    for r in range(T):
+        t = q_pos0 + r
+        vis = [j for j in range(kv_comp.shape[0]) if all(ratio * j + m <= t for m in range(ratio))]
+        score = {}
+        for j in vis:
+            total = 0
+            for h in range(Hi):
+                dot = sum(int(iq[r, h, d]) * int(ik[j, d]) for d in range(Di))
+                total += int(iw[r, h]) * max(dot, 0)
+            score[j] = total
+        chosen = sorted(vis, key=lambda j: (-score[j], j))[:top_k]
+        sels.append(chosen + [-1] * (top_k - len(chosen)))
+        keys = [kv_comp[j] for j in chosen] + [kv_raw[s] for s in range(t + 1) if t - s < window]
+        o_t, l_t = [], []
+        for h in range(H):
+            z = [scale * sum(float(q[r, h, d]) * float(key[d]) for d in range(D)) for key in keys]
+            m = max(z)
+            e = [math.exp(v - m) for v in z]
+            den = sum(e)
+            o_t.append([sum(e[i] * float(keys[i][c]) for i in range(len(keys))) / den for c in range(d_v)])
+            l_t.append(m + math.log(den))
+        outs.append(o_t)
+        lses.append(l_t)
+    return sels, outs, lses
+
+
+def pin_prefill_end_to_end(orc):
+    """The oracle's whole-layer entry point (the one the GPU path is compared
+    with) against the plain-Python layer above: indexer, top-k and attention
+    composed with the right arguments and query offsets, over several
+    chunks of a call that starts mid-sequence, and over a sub-range of its
+    queries. Window and top-k differ, so passing one for the other fails."""
+    rng = np.random.default_rng(19)
+    n_q, q_pos0, ratio = 13, 7, 4
+    inp = _tiny_inputs(rng, n_q=n_q, q_pos0=q_pos0, ratio=ratio, H=2, D=6, Hi=3, Di=5)
+    kw = dict(ratio=ratio, window=3, top_k=2, scale=0.41, d_v=4)
+    sels, outs, lses = _prefill_brute(inp, q_pos0, **kw)
+    full = orc.prefill(inp, q_pos0=q_pos0, chunk=5, **kw)
+    np.testing.assert_array_equal(full["sel"], np.array(sels, dtype=np.int64))
+    np.testing.assert_array_equal(full["n_sel"], [sum(1 for j in s if j >= 0) for s in sels])
+    np.testing.assert_allclose(full["out"], np.array(outs), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(full["lse"], np.array(lses), rtol=0, atol=1e-12)
+    part = orc.prefill(inp, q_pos0=q_pos0, q_begin=4, q_end=11, chunk=3, **kw)
+    np.testing.assert_array_equal(part["sel"], np.array(sels[4:11], dtype=np.int64))
+    np.testing.assert_allclose(part["out"], np.array(outs[4:11]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(part["lse"], np.array(lses[4:11]), rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------ compression pins
 def _fp16_bits_exact(v):
     """IEEE binary16 bits of the exact rational v rounded to nearest, ties
@@ -499,6 +557,7 @@ PINS = [
     pin_attention_closed_forms,
     pin_sparse_equals_dense_sdpa,
     pin_band_independence,
+    pin_prefill_end_to_end,
     pin_compress_exact_rounding,
     pin_compress_closed_forms,
 ]

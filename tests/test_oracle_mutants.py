@@ -59,6 +59,15 @@ MUTANTS = [
      "    total = groups.sum(axis=1)"),
     ("prefill-query-offset", "indexer_scores(iq[a:b], iw[a:b], ik, q_pos0 + a, ratio)",
      "indexer_scores(iq[a:b], iw[a:b], ik, q_pos0, ratio)"),
+    ("prefill-topk-offset", "topk_select(sc, q_pos0 + a, ratio, top_k, n_comp)",
+     "topk_select(sc, q_pos0, ratio, top_k, n_comp)"),
+    ("prefill-topk-gets-window", "topk_select(sc, q_pos0 + a, ratio, top_k, n_comp)",
+     "topk_select(sc, q_pos0 + a, ratio, window, n_comp)"),
+    ("prefill-attn-offset", "sel, n_sel, q_pos0 + a,\n", "sel, n_sel, q_pos0,\n"),
+    ("prefill-attn-gets-top-k", "                                    window, scale, d_v)",
+     "                                    top_k, scale, d_v)"),
+    ("prefill-ignores-q-begin", "for a in range(q_begin, q_end, chunk):", "for a in range(0, q_end - q_begin, chunk):"),
+    ("prefill-chunk-overlap", "b = min(q_end, a + chunk)", "b = min(q_end, a + chunk + 1)"),
 ]
 
 
