@@ -390,11 +390,14 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   }
   __syncthreads();
   // Ascending order (optional): the winners' rows are marked in a bitmap of
-  // the visible rows (nv <= kMaxComp bits) laid over keys[], which is free
-  // once scattered, and read back in row order after a block-wide scan of
-  // the words' popcounts.
-  unsigned* const bits = reinterpret_cast<unsigned*>(keys);
+  // the visible rows (nv <= kMaxComp bits) and read back in row order after
+  // a block-wide scan of the words' popcounts. The bitmap takes keys[0, cap),
+  // which is free once scattered, when it fits there (2 * cap words);
+  // otherwise it follows the bucketed copy, where the launcher reserves
+  // asc_bitmap_words(n_comp, cap) words. It never overlaps the bucketed keys,
+  // which the placement below still reads.
   const int nwords = (nv + 31) >> 5;
+  unsigned* const bits = reinterpret_cast<unsigned*>(nwords <= 2 * cap ? keys : keys + 2 * cap);
   if (a.sel_asc) {
     for (int i = tid; i < nwords; i += BLOCK) bits[i] = 0u;
     __syncthreads();
@@ -470,10 +473,28 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a, FusedArgs f) {
   }
 }
 
+// Words of LDS reserved after the bucketed keys for the ascending-order
+// bitmap: none when a bitmap of every visible row (at most n_comp) fits in
+// the 2 * cap words of the collected keys, which are free by then.
+size_t asc_bitmap_words(int n_comp, int cap) {
+  const size_t words = ((size_t)n_comp + 31) / 32;
+  return words <= 2 * (size_t)cap ? 0 : words;
+}
+
 template <int BLOCK, int PER, int SRC>
 hipError_t launch_cfg(const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
-  // keys: the collected elements (at most top_k + kSlack) and their bucketed copy.
-  const size_t lds = 2 * sizeof(u64) * (size_t)std::min(a.top_k + kSlack, BLOCK * PER);
+  // keys: the collected elements (at most top_k + kSlack) and their bucketed
+  // copy, then the ascending-order bitmap when it does not fit over the first.
+  const int cap = std::min(a.top_k + kSlack, BLOCK * PER);
+  size_t lds = 2 * sizeof(u64) * (size_t)cap;
+  if (a.sel_asc) {
+    const size_t extra = asc_bitmap_words(a.n_comp, cap);
+    lds += sizeof(unsigned) * extra;
+    // Every token sees at most n_comp rows: its bitmap of ceil(nv / 32)
+    // words fits wherever the kernel puts it.
+    const size_t words = ((size_t)a.n_comp + 31) / 32;
+    if (!(words <= 2 * (size_t)cap || extra >= words)) return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL((topk_kernel<BLOCK, PER, SRC>), dim3(grid), dim3(BLOCK), lds, stream, a, f);
   return hipGetLastError();
 }

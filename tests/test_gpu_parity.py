@@ -3,8 +3,7 @@
 Bar: selected indices and indexer scores bit-exact; attention outputs within
 max-abs 2e-3 and NMSE 1e-6 of the fp64 oracle over each compared tensor.
 Full-size workloads run in the same launch configuration as the benchmark
-(spmla_prefill, 2,048-query bands) and are compared on sampled queries that
-the oracle computes one by one.
+(spmla_prefill, 2,048-query bands) and are compared whole.
 """
 import math
 import sys
@@ -115,49 +114,21 @@ def test_prefill_matches_oracle(sp, name):
     assert_close(lse.cpu().numpy(), ref["lse"], f"{name} lse")
 
 
-# ------------------------------------------------------ full size, sampled
-def sample_rows(w, n=48, seed=0):
-    rng = np.random.default_rng(1000 + seed)
-    rows = {0, 1, 2, 3, 4, w.n_q - 1, w.n_q - 2}
-    for b in range(0, w.n_q, w.band):  # both sides of every band edge
-        rows.update({b, max(0, b - 1), min(w.n_q - 1, b + 1)})
-    rows.update(int(v) for v in rng.integers(0, w.n_q, n))
-    return sorted(r for r in rows if 0 <= r < w.n_q)
+# ------------------------------------------------------- full size, whole
+WHOLE = ["prefill-8192", "prefill-9133", "prefill-10240", "chunk-8192-after-114687"]
 
 
-@pytest.mark.parametrize("name", ["prefill-8192", "prefill-9133", "chunk-8192-after-114687"])
-def test_full_size_prefill_sampled(sp, name):
-    import torch
-
-    w = workloads.BY_NAME[name]
-    say(f"[parity full] {name}: generating")
-    x = workloads.generate(w)
-    dev = to_dev(x)
-    say(f"[parity full] {name}: running spmla_prefill")
-    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
-    torch.cuda.synchronize()
-    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
-    rows = sample_rows(w)
-    say(f"[parity full] {name}: oracle on {len(rows)} sampled queries")
-    want_out, want_lse, got_out, got_lse = [], [], [], []
-    for r in rows:
-        ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
-                             scale=w.scale, d_v=w.d_v, q_begin=r, q_end=r + 1)
-        np.testing.assert_array_equal(sel[r], ref["sel"][0], err_msg=f"sel row {r}")
-        want_out.append(ref["out"][0]), want_lse.append(ref["lse"][0])
-        got_out.append(out[r]), got_lse.append(lse[r])
-    assert_close(np.array(got_out), np.array(want_out), f"{name} out[sampled]")
-    assert_close(np.array(got_lse), np.array(want_lse), f"{name} lse[sampled]")
-
-
-@pytest.mark.parametrize("name", ["prefill-8192", "prefill-9133"])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", WHOLE)
 def test_prefill_whole_tensor(sp, name):
-    """The benchmarked workload (and the 9,133-token one, five bands with a
-    ragged last) in the benchmarked launch configuration, compared whole:
-    every selected index of every query bit-exact, and out and lse within
-    max-abs 2e-3 and NMSE 1e-6 over the entire tensors (the oracle computes
-    a whole layer in about 10 s on 16 host cores)."""
+    """Every full-size workload in the benchmarked launch configuration
+    (spmla_prefill, 2,048-query bands), compared whole: every selected index
+    of every query bit-exact, and out and lse within max-abs 2e-3 and NMSE
+    1e-6 over the entire tensors. prefill-8192 is the benchmarked workload,
+    prefill-9133 has five bands with a ragged last, prefill-10240 is the
+    five-band frontier, and the long-context chunk (8,192 queries after
+    114,687 tokens, 30,719 compressed rows) runs the fused selection and the
+    ascending-row handoff; its oracle takes about a minute."""
     import time
 
     import torch
@@ -171,6 +142,8 @@ def test_prefill_whole_tensor(sp, name):
     torch.cuda.synchronize()
     out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
     del dev
+    torch.cuda.empty_cache()
+    say(f"[parity whole] {w.name}: oracle")
     t0 = time.perf_counter()
     ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
                          scale=w.scale, d_v=w.d_v)
@@ -487,6 +460,53 @@ def test_edge_cases(sp, name, w):
     assert_close(o2.cpu().numpy(), ref["out"], f"{name} prefill out")
 
 
+SMALL_K_LONG = [(k, n_q, q_pos0) for k, q_pos0 in ((1, 130000), (32, 100000), (100, 80000), (271, 127000))
+                for n_q in (64, 300)]
+
+
+@pytest.mark.parametrize("top_k,n_q,q_pos0", SMALL_K_LONG, ids=[f"k{k}-nq{n}" for k, n, _ in SMALL_K_LONG])
+def test_small_topk_long_history(sp, top_k, n_q, q_pos0):
+    """Small top-k over 20-32K compressed rows, where the selection is also
+    handed to attention in ascending row order (compressed rows beyond
+    4 MiB): the order bitmap of up to 1,024 words must not overlap the keys
+    the ordering pass still reads. 64 queries take the score-matrix
+    selection, 300 the fused handoff; every index bit-exact."""
+    import torch
+
+    w = workloads.LayerShape(f"smallk{top_k}", n_q=n_q, q_pos0=q_pos0, window=128, top_k=top_k)
+    say(f"[parity small-k] top_k={top_k} n_q={n_q} q_pos0={q_pos0} n_comp={w.n_comp}")
+    x = workloads.generate(w, seed=40 + top_k)
+    dev = to_dev(x)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"{w.name} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"{w.name} lse")
+
+
+def test_largest_topk_long_history(sp):
+    """top_k 4,096 (the largest supported) over 32,500 compressed rows: the
+    top-k workgroup holds 4,336 collected keys and their bucketed copy."""
+    import torch
+
+    w = workloads.LayerShape("k4096", n_q=17, q_pos0=130000 - 17, window=128, top_k=4096)
+    say(f"[parity] top_k=4096 n_q={w.n_q} n_comp={w.n_comp}")
+    x = workloads.generate(w, seed=50)
+    dev = to_dev(x)
+    scores, sel, n_sel, out, lse = run_steps(sp, w, x, dev)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    np.testing.assert_array_equal(sel, ref["sel"])
+    np.testing.assert_array_equal(n_sel, ref["n_sel"])
+    assert_close(out, ref["out"], f"{w.name} out")
+    o2, l2, s2 = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s2.cpu().numpy(), ref["sel"])
+    assert_close(o2.cpu().numpy(), ref["out"], f"{w.name} prefill out")
+
+
 def random_shapes(n_small=12, n_large=4, seed=2024):
     """Seeded random descriptors: 1-300 queries (key-split attention) and
     513-900 queries (whole-query attention), positions up to 6,000, windows
@@ -501,7 +521,24 @@ def random_shapes(n_small=12, n_large=4, seed=2024):
     return shapes
 
 
-RANDOM = random_shapes()
+def random_long_shapes(n=10, seed=2025):
+    """Seeded random descriptors over long histories (positions up to
+    131,000, so up to 32,750 compressed rows): 1-600 queries, top-k 1-2,048,
+    windows 1-200 and bands of 37-2,048 queries, so that calls reach the
+    fused selection (bands of at least 256 queries) and the ascending-row
+    handoff (more than 3,641 compressed rows)."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        n_q = int(rng.choice([1, 5, 64, 255, 256, 300, 600]))
+        shapes.append(workloads.LayerShape(
+            f"long{i}", n_q=n_q, q_pos0=int(rng.integers(4000, 131000 - n_q)),
+            window=int(rng.choice([1, 16, 128, 200])), top_k=int(rng.choice([1, 7, 32, 100, 271, 512, 1024, 2048])),
+            band=int(rng.choice([37, 256, 300, 2048]))))
+    return shapes
+
+
+RANDOM = random_shapes() + random_long_shapes()
 
 
 @pytest.mark.parametrize("w", RANDOM, ids=[w.name for w in RANDOM])

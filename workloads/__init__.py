@@ -82,7 +82,11 @@ CHUNK_8192_AT_114687 = LayerShape(
 DECODE_1 = LayerShape("decode-1-at-122878", n_q=1, q_pos0=122878, window=128, top_k=2048)
 VERIFY_5 = LayerShape("verify-5-at-122874", n_q=5, q_pos0=122874, window=128, top_k=2048)
 
-WORKLOADS = [TINY_256, BAND_2048, PREFILL_8192, PREFILL_9133, CHUNK_8192_AT_114687, DECODE_1, VERIFY_5]
+# The five-band frontier: five full 2,048-token bands, 10,240 tokens.
+PREFILL_10240 = LayerShape("prefill-10240", n_q=10240, q_pos0=0, window=128, top_k=512)
+
+WORKLOADS = [TINY_256, BAND_2048, PREFILL_8192, PREFILL_9133, CHUNK_8192_AT_114687, DECODE_1, VERIFY_5,
+             PREFILL_10240]
 BY_NAME = {w.name: w for w in WORKLOADS}
 # Seed of each named workload: its position in WORKLOADS.
 SEEDS = {w.name: i for i, w in enumerate(WORKLOADS)}
