@@ -247,6 +247,32 @@ int spmla_prefill(const spmla_desc* desc, const uint16_t* q, const uint16_t* kv_
                   float* out, float* lse, int32_t* sel_out, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * spmla_prefill without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same inputs, outputs and results
+ * as spmla_prefill (bit for bit: the schedule below only changes how
+ * queries are grouped into launches, and results do not depend on it).
+ *
+ * Scratch: a 64 MiB array in the library's device image (one per GPU that
+ * loads the library, held until the process ends); its device address is
+ * looked up on the first call on each device. The call allocates nothing
+ * and calls no allocating routine. Selection groups hold at most 32 MiB of
+ * scratch each, and when a call's scratch would still exceed 64 MiB its
+ * bands are halved until it fits (e.g. the 8,192 queries after 114,687
+ * tokens run in bands of 512). Returns SPMLA_EWORKSPACE, with nothing
+ * enqueued, if even one-query bands do not fit.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (several streams, or several host threads) race and corrupt each
+ * other; the caller orders them, e.g. on one stream. The array keeps the
+ * last call's contents; no part of it needs to start at zero. `stream`
+ * must belong to the current device (else SPMLA_EINVAL).
+ */
+int spmla_prefill_noalloc(const spmla_desc* desc, const uint16_t* q, const uint16_t* kv_comp,
+                          const uint16_t* kv_raw, const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                          float* out, float* lse, int32_t* sel_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,7 @@ __all__ = [
     "spmla_compress",
     "spmla_prefill_workspace_bytes",
     "spmla_prefill",
+    "spmla_prefill_noalloc",
     "prefill",
     "EXPORTED_SYMBOLS",
 ]
@@ -54,6 +55,7 @@ EXPORTED_SYMBOLS = [
     "spmla_compress",
     "spmla_prefill_workspace_bytes",
     "spmla_prefill",
+    "spmla_prefill_noalloc",
 ]
 
 
@@ -120,6 +122,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spmla_compress": (ctypes.c_int, [D, P, P, ctypes.c_int32, P]),
         "spmla_prefill_workspace_bytes": (ctypes.c_int, [D, ctypes.POINTER(ctypes.c_size_t)]),
         "spmla_prefill": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "spmla_prefill_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -283,6 +286,18 @@ def spmla_prefill(desc, q, kv_comp, kv_raw, iq, iw, ik, out, lse, sel_out, works
                (out, torch.float32, "out", _n(desc, "out")), (lse, torch.float32, "lse", _n(desc, "lse")),
                (sel_out, torch.int32, "sel_out", _n(desc, "sel")), (workspace, None, "workspace", 0)),
         ctypes.c_size_t(workspace_bytes), _stream(stream)))
+
+
+def spmla_prefill_noalloc(desc, q, kv_comp, kv_raw, iq, iw, ik, out, lse, sel_out, stream=None) -> None:
+    torch = _dt()
+    _check(load_library().spmla_prefill_noalloc(
+        ctypes.byref(desc),
+        *_ptrs((q, torch.float16, "q", _n(desc, "q")), (kv_comp, torch.float16, "kv_comp", _n(desc, "kv_comp")),
+               (kv_raw, torch.float16, "kv_raw", _n(desc, "kv_raw")), (iq, torch.int8, "iq", _n(desc, "iq")),
+               (iw, torch.int8, "iw", _n(desc, "iw")), (ik, torch.int8, "ik", _n(desc, "ik")),
+               (out, torch.float32, "out", _n(desc, "out")), (lse, torch.float32, "lse", _n(desc, "lse")),
+               (sel_out, torch.int32, "sel_out", _n(desc, "sel"))),
+        _stream(stream)))
 
 
 def prefill(desc, dev: dict, want_sel=True, want_lse=True, stream=None):

@@ -96,8 +96,11 @@ constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator 
 // handoff's thresholds, slot counts and candidate slots (512 MiB). The
 // attention still runs band by band. One launch per step instead of one per
 // band removes the ramp and tail of short, latency-bound launches.
-constexpr size_t kSelGroupBytes = (size_t)128 << 20;
-constexpr size_t kFusedGroupBytes = (size_t)512 << 20;
+struct GroupBudget {
+  size_t dense;  // score-matrix bytes of one group
+  size_t fused;  // fused-handoff scratch bytes of one group
+};
+constexpr GroupBudget kGroupBudget{(size_t)128 << 20, (size_t)512 << 20};
 int64_t group_rows_within(const spmla_desc* d, size_t per_band, size_t budget) {
   const int64_t band_rows = d->band < d->n_q ? d->band : d->n_q;
   int64_t bands = per_band ? (int64_t)(budget / per_band) : INT64_MAX / 2 / (band_rows > 0 ? band_rows : 1);
@@ -105,11 +108,13 @@ int64_t group_rows_within(const spmla_desc* d, size_t per_band, size_t budget) {
   const int64_t rows = bands * band_rows;
   return rows < d->n_q ? rows : d->n_q;
 }
-int64_t dense_group_rows(const spmla_desc* d) { return group_rows_within(d, scores_bytes_per_band(d), kSelGroupBytes); }
-int64_t fused_group_rows(const spmla_desc* d) {
+int64_t dense_group_rows(const spmla_desc* d, const GroupBudget& gb) {
+  return group_rows_within(d, scores_bytes_per_band(d), gb.dense);
+}
+int64_t fused_group_rows(const spmla_desc* d, const GroupBudget& gb) {
   const int band_rows = d->band < d->n_q ? d->band : d->n_q;
   const spmla::FusedPlan plan = spmla::fused_plan(d->n_comp, d->top_k);
-  return group_rows_within(d, spmla::fused_workspace_bytes(band_rows, plan), kFusedGroupBytes);
+  return group_rows_within(d, spmla::fused_workspace_bytes(band_rows, plan), gb.fused);
 }
 int band_len(const spmla_desc* d, int64_t b0) { return (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band); }
 bool fused_band(const spmla_desc* d, int64_t b0) {
@@ -121,8 +126,8 @@ bool fused_band(const spmla_desc* d, int64_t b0) {
 // that way's budget. spmla_prefill runs exactly these groups, and the
 // workspace is sized from them.
 template <typename F>
-void for_each_group(const spmla_desc* d, F&& f) {
-  const int64_t dense_cap = dense_group_rows(d), fused_cap = fused_group_rows(d);
+void for_each_group(const spmla_desc* d, const GroupBudget& gb, F&& f) {
+  const int64_t dense_cap = dense_group_rows(d, gb), fused_cap = fused_group_rows(d, gb);
   for (int64_t g0 = 0; g0 < d->n_q;) {
     const bool fused = fused_band(d, g0);
     const int64_t cap = fused ? fused_cap : dense_cap;  // a multiple of the band unless it covers every query
@@ -143,12 +148,12 @@ struct WsLayout {
   size_t sel = 0;  // bytes of one selection copy
   size_t total() const { return scratch + 2 * sel; }
 };
-WsLayout ws_layout(const spmla_desc* d) {
+WsLayout ws_layout(const spmla_desc* d, const GroupBudget& gb) {
   WsLayout w;
   const int band_rows = d->band < d->n_q ? d->band : d->n_q;
   w.scratch = round_up(spmla::attn_partial_bytes(band_rows, spmla::attn_splits(d->n_q)), 256);
   int64_t max_rows = 0;
-  for_each_group(d, [&](int64_t g0, int64_t g1, bool fused) {
+  for_each_group(d, gb, [&](int64_t g0, int64_t g1, bool fused) {
     const int64_t rows = g1 - g0;
     const size_t need = fused ? spmla::fused_workspace_bytes((int)rows, spmla::fused_plan(d->n_comp, d->top_k))
                               : round_up((size_t)rows * (size_t)band_ld(d) * sizeof(int32_t), 256);
@@ -180,6 +185,102 @@ spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t
   a.part_o = nullptr;
   a.part_ml = nullptr;
   return a;
+}
+
+// Steps 1-4 of a checked call: selection per group, attention per band, all
+// enqueued on `st`. `ws` holds at least ws_layout(d, gb).total() bytes.
+int run_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp, const uint16_t* kv_raw,
+                const int8_t* iq, const int8_t* iw, const int8_t* ik, float* out, float* lse, int32_t* sel_out,
+                char* ws, const GroupBudget& gb, hipStream_t st) {
+  int rc = SPMLA_OK;
+  const WsLayout lay = ws_layout(d, gb);
+  int32_t* scores = reinterpret_cast<int32_t*>(ws);
+  int32_t* ws_sel = reinterpret_cast<int32_t*>(ws + lay.scratch);
+  int32_t* ws_sel_asc = reinterpret_cast<int32_t*>(ws + lay.scratch + lay.sel);
+  // Attention takes each selection in ascending row order when the
+  // compressed rows outgrow one die's L2: the queries in flight on a die then
+  // sweep the rows together and share what they gather (the softmax does not
+  // depend on the order of its keys).
+  const bool ascending = (size_t)d->n_comp * kRowBytes > kDieL2Bytes;
+
+  for_each_group(d, gb, [&](int64_t g0, int64_t g1, bool fused) {
+    if (rc) return;
+    const int gn = (int)(g1 - g0);
+    const int gpos0 = d->q_pos0 + (int)g0;
+    // The group's selections: rows g0 .. g1-1 of sel_out, or the workspace.
+    int32_t* gsel = sel_out ? sel_out + g0 * d->top_k : ws_sel;
+    if (fused) {
+      // Long history: indexer -> top-k handoff without the score matrix.
+      spmla::FusedArgs fa{};
+      fa.iq = iq + g0 * spmla::kIdxHeads * spmla::kIdxDim;
+      fa.iw = iw + g0 * spmla::kIdxHeads;
+      fa.ik = ik;
+      fa.sel = gsel;
+      fa.n_sel = nullptr;
+      fa.sel_asc = ascending ? ws_sel_asc : nullptr;
+      fa.n_q = gn;
+      fa.q_pos0 = gpos0;
+      fa.n_comp = d->n_comp;
+      fa.ratio = d->ratio;
+      fa.top_k = d->top_k;
+      fa.plan = spmla::fused_plan(d->n_comp, d->top_k);
+      spmla::fused_bind_workspace(fa, ws);
+      rc = hip_status(spmla::launch_fused_topk(fa, st), "fused selection launch");
+      if (rc) return;
+    } else {
+      if (d->n_comp > 0) {
+        spmla::IndexerArgs ia;
+        ia.iq = iq + g0 * spmla::kIdxHeads * spmla::kIdxDim;
+        ia.iw = iw + g0 * spmla::kIdxHeads;
+        ia.ik = ik;
+        ia.scores = scores;
+        ia.ld_scores = band_ld(d);
+        ia.n_q = gn;
+        ia.q_pos0 = gpos0;
+        ia.n_comp = d->n_comp;
+        ia.ratio = d->ratio;
+        ia.fill_invisible = 0;  // top-k reads only the rows each token can see
+        ia.span = 0;
+        rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
+        if (rc) return;
+      }
+      spmla::TopkArgs ta;
+      ta.scores = scores;
+      ta.ld_scores = band_ld(d);
+      ta.sel = gsel;
+      ta.n_sel = nullptr;
+      ta.sel_asc = ascending ? ws_sel_asc : nullptr;
+      ta.n_q = gn;
+      ta.q_pos0 = gpos0;
+      ta.n_comp = d->n_comp;
+      ta.ratio = d->ratio;
+      ta.top_k = d->top_k;
+      rc = hip_status(spmla::launch_topk(ta, st), "top-k launch");
+      if (rc) return;
+    }
+
+    // Attention band by band.
+    for (int64_t b0 = g0; b0 < g1; b0 += d->band) {
+      const int bn = band_len(d, b0);
+      const int64_t row = b0 - g0;  // first row of this band's selections within the group
+      const int32_t* sel = ascending ? ws_sel_asc + row * d->top_k : gsel + row * d->top_k;
+      spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
+                                     out + b0 * spmla::kHeads * spmla::kDv,
+                                     lse ? lse + b0 * spmla::kHeads : nullptr);
+      aa.n_q = bn;
+      aa.q_pos0 = d->q_pos0 + (int)b0;
+      aa.splits = spmla::attn_splits(d->n_q);
+      if (aa.splits > 1) {  // a small call: split each key list, partials in the scratch
+        const size_t items = (size_t)bn * aa.splits;
+        aa.part_o = reinterpret_cast<float*>(ws);
+        aa.part_ml = aa.part_o + items * spmla::kHeads * spmla::kDv;
+      }
+      rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
+      if (rc) return;
+    }
+  });
+  if (rc) return rc;
+  return ok();
 }
 
 }  // namespace
@@ -300,7 +401,7 @@ int spmla_prefill_workspace_bytes(const spmla_desc* d, size_t* bytes) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (!bytes) return fail(SPMLA_EINVAL, "bytes is NULL");
-  *bytes = ws_layout(d).total();
+  *bytes = ws_layout(d, kGroupBudget).total();
   return ok();
 }
 
@@ -328,96 +429,52 @@ int spmla_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_com
     return fail(SPMLA_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
   REQUIRE_PTR(workspace);
 
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = static_cast<char*>(workspace);
-  const WsLayout lay = ws_layout(d);
-  int32_t* scores = reinterpret_cast<int32_t*>(ws);
-  int32_t* ws_sel = reinterpret_cast<int32_t*>(ws + lay.scratch);
-  int32_t* ws_sel_asc = reinterpret_cast<int32_t*>(ws + lay.scratch + lay.sel);
-  // Attention takes each selection in ascending row order when the
-  // compressed rows outgrow one die's L2: the queries in flight on a die then
-  // sweep the rows together and share what they gather (the softmax does not
-  // depend on the order of its keys).
-  const bool ascending = (size_t)d->n_comp * kRowBytes > kDieL2Bytes;
+  return run_prefill(d, q, kv_comp, kv_raw, iq, iw, ik, out, lse, sel_out, static_cast<char*>(workspace),
+                     kGroupBudget, (hipStream_t)stream);
+}
 
-  for_each_group(d, [&](int64_t g0, int64_t g1, bool fused) {
-    if (rc) return;
-    const int gn = (int)(g1 - g0);
-    const int gpos0 = d->q_pos0 + (int)g0;
-    // The group's selections: rows g0 .. g1-1 of sel_out, or the workspace.
-    int32_t* gsel = sel_out ? sel_out + g0 * d->top_k : ws_sel;
-    if (fused) {
-      // Long history: indexer -> top-k handoff without the score matrix.
-      spmla::FusedArgs fa{};
-      fa.iq = iq + g0 * spmla::kIdxHeads * spmla::kIdxDim;
-      fa.iw = iw + g0 * spmla::kIdxHeads;
-      fa.ik = ik;
-      fa.sel = gsel;
-      fa.n_sel = nullptr;
-      fa.sel_asc = ascending ? ws_sel_asc : nullptr;
-      fa.n_q = gn;
-      fa.q_pos0 = gpos0;
-      fa.n_comp = d->n_comp;
-      fa.ratio = d->ratio;
-      fa.top_k = d->top_k;
-      fa.plan = spmla::fused_plan(d->n_comp, d->top_k);
-      spmla::fused_bind_workspace(fa, ws);
-      rc = hip_status(spmla::launch_fused_topk(fa, st), "fused selection launch");
-      if (rc) return;
-    } else {
-      if (d->n_comp > 0) {
-        spmla::IndexerArgs ia;
-        ia.iq = iq + g0 * spmla::kIdxHeads * spmla::kIdxDim;
-        ia.iw = iw + g0 * spmla::kIdxHeads;
-        ia.ik = ik;
-        ia.scores = scores;
-        ia.ld_scores = band_ld(d);
-        ia.n_q = gn;
-        ia.q_pos0 = gpos0;
-        ia.n_comp = d->n_comp;
-        ia.ratio = d->ratio;
-        ia.fill_invisible = 0;  // top-k reads only the rows each token can see
-        ia.span = 0;
-        rc = hip_status(spmla::launch_indexer(ia, st), "indexer launch");
-        if (rc) return;
-      }
-      spmla::TopkArgs ta;
-      ta.scores = scores;
-      ta.ld_scores = band_ld(d);
-      ta.sel = gsel;
-      ta.n_sel = nullptr;
-      ta.sel_asc = ascending ? ws_sel_asc : nullptr;
-      ta.n_q = gn;
-      ta.q_pos0 = gpos0;
-      ta.n_comp = d->n_comp;
-      ta.ratio = d->ratio;
-      ta.top_k = d->top_k;
-      rc = hip_status(spmla::launch_topk(ta, st), "top-k launch");
-      if (rc) return;
-    }
-
-    // Attention band by band.
-    for (int64_t b0 = g0; b0 < g1; b0 += d->band) {
-      const int bn = band_len(d, b0);
-      const int64_t row = b0 - g0;  // first row of this band's selections within the group
-      const int32_t* sel = ascending ? ws_sel_asc + row * d->top_k : gsel + row * d->top_k;
-      spmla::AttnArgs aa = attn_args(d, q + b0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
-                                     out + b0 * spmla::kHeads * spmla::kDv,
-                                     lse ? lse + b0 * spmla::kHeads : nullptr);
-      aa.n_q = bn;
-      aa.q_pos0 = d->q_pos0 + (int)b0;
-      aa.splits = spmla::attn_splits(d->n_q);
-      if (aa.splits > 1) {  // a small call: split each key list, partials in the scratch
-        const size_t items = (size_t)bn * aa.splits;
-        aa.part_o = reinterpret_cast<float*>(ws);
-        aa.part_ml = aa.part_o + items * spmla::kHeads * spmla::kDv;
-      }
-      rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
-      if (rc) return;
-    }
-  });
+int spmla_prefill_noalloc(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
+                          const uint16_t* kv_raw, const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                          float* out, float* lse, int32_t* sel_out, void* stream) {
+  int rc = check_desc(d);
   if (rc) return rc;
-  return ok();
+  if (d->n_q == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv_raw);
+  REQUIRE_PTR(iq);
+  REQUIRE_PTR(iw);
+  if (d->n_comp > 0) {
+    REQUIRE_PTR(kv_comp);
+    REQUIRE_PTR(ik);
+  }
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(lse);
+  OPTIONAL_PTR(sel_out);
+  // Selection groups of at most half the scratch each; bands halve until the
+  // call's scratch fits (results do not depend on the band).
+  const size_t cap = spmla::kNoAllocScratchBytes;
+  const GroupBudget gb{cap / 2, cap / 2};
+  spmla_desc dd = *d;
+  size_t need = ws_layout(&dd, gb).total();
+  while (need > cap && dd.band > 1) {
+    dd.band = (dd.band + 1) / 2;
+    need = ws_layout(&dd, gb).total();
+  }
+  if (need > cap)
+    return fail(SPMLA_EWORKSPACE, "needs %zu bytes of scratch even at band %d; the no-alloc scratch holds %zu",
+                need, dd.band, cap);
+  // The scratch is per device: the stream must run on the current device.
+  int cur = -1, sdev = -1;
+  rc = hip_status(hipGetDevice(&cur), "current device");
+  if (rc) return rc;
+  rc = hip_status(hipStreamGetDevice((hipStream_t)stream, &sdev), "device of the stream");
+  if (rc) return rc;
+  if (sdev != cur) return fail(SPMLA_EINVAL, "stream is on device %d, the current device is %d", sdev, cur);
+  void* scratch = nullptr;
+  rc = hip_status(spmla::noalloc_scratch(&scratch), "no-alloc scratch address");
+  if (rc) return rc;
+  return run_prefill(&dd, q, kv_comp, kv_raw, iq, iw, ik, out, lse, sel_out, static_cast<char*>(scratch), gb,
+                     (hipStream_t)stream);
 }
 
 }  // extern "C"

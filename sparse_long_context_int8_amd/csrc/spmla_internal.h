@@ -135,4 +135,9 @@ hipError_t launch_attn_grouped(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_compress(const uint16_t* kv_raw, uint16_t* kv_comp, int comp_begin, int n_comp,
                            hipStream_t stream);
 
+// Bytes of the device-resident scratch array of spmla_prefill_noalloc, and
+// its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace spmla
