@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libspmla.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attn.hip", "compress.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "indexer.hip", "topk.hip", "attn.hip", "compress.hip", "noalloc.hip"]
 ARCH = "gfx950"
 # Per-source code generation options. The int8 indexer kernels consume every
 # matrix-core result with vector ops at once; the VGPR form of the MFMA

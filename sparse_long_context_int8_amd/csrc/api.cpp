@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 
@@ -99,22 +100,26 @@ constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator 
 struct GroupBudget {
   size_t dense;  // score-matrix bytes of one group
   size_t fused;  // fused-handoff scratch bytes of one group
+  size_t sel;    // bytes of a group's two selection copies (score and row order)
 };
-constexpr GroupBudget kGroupBudget{(size_t)128 << 20, (size_t)512 << 20};
-int64_t group_rows_within(const spmla_desc* d, size_t per_band, size_t budget) {
+constexpr GroupBudget kGroupBudget{(size_t)128 << 20, (size_t)512 << 20, SIZE_MAX};
+int64_t group_rows_within(const spmla_desc* d, size_t per_band, size_t budget, size_t sel_budget) {
   const int64_t band_rows = d->band < d->n_q ? d->band : d->n_q;
+  const size_t sel_per_band = 2 * (size_t)band_rows * (size_t)d->top_k * sizeof(int32_t);
   int64_t bands = per_band ? (int64_t)(budget / per_band) : INT64_MAX / 2 / (band_rows > 0 ? band_rows : 1);
+  if (sel_budget != SIZE_MAX && sel_per_band > 0 && (int64_t)(sel_budget / sel_per_band) < bands)
+    bands = (int64_t)(sel_budget / sel_per_band);
   if (bands < 1) bands = 1;
   const int64_t rows = bands * band_rows;
   return rows < d->n_q ? rows : d->n_q;
 }
 int64_t dense_group_rows(const spmla_desc* d, const GroupBudget& gb) {
-  return group_rows_within(d, scores_bytes_per_band(d), gb.dense);
+  return group_rows_within(d, scores_bytes_per_band(d), gb.dense, gb.sel);
 }
 int64_t fused_group_rows(const spmla_desc* d, const GroupBudget& gb) {
   const int band_rows = d->band < d->n_q ? d->band : d->n_q;
   const spmla::FusedPlan plan = spmla::fused_plan(d->n_comp, d->top_k);
-  return group_rows_within(d, spmla::fused_workspace_bytes(band_rows, plan), gb.fused);
+  return group_rows_within(d, spmla::fused_workspace_bytes(band_rows, plan), gb.fused, gb.sel);
 }
 int band_len(const spmla_desc* d, int64_t b0) { return (int)((d->n_q - b0) < d->band ? (d->n_q - b0) : d->band); }
 bool fused_band(const spmla_desc* d, int64_t b0) {
@@ -450,10 +455,11 @@ int spmla_prefill_noalloc(const spmla_desc* d, const uint16_t* q, const uint16_t
   REQUIRE_PTR(out);
   OPTIONAL_PTR(lse);
   OPTIONAL_PTR(sel_out);
-  // Selection groups of at most half the scratch each; bands halve until the
-  // call's scratch fits (results do not depend on the band).
+  // Selection groups whose selection scratch and selection copies each take
+  // at most half the array; bands halve until the call's scratch fits
+  // (results do not depend on the band).
   const size_t cap = spmla::kNoAllocScratchBytes;
-  const GroupBudget gb{cap / 2, cap / 2};
+  const GroupBudget gb{cap / 2, cap / 2, cap / 2};
   spmla_desc dd = *d;
   size_t need = ws_layout(&dd, gb).total();
   while (need > cap && dd.band > 1) {

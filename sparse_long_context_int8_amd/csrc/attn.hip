@@ -874,7 +874,6 @@ void attn_kernel(AttnArgs a) {
 // fourth split (8 loads in flight per thread) and meet in LDS in a fixed
 // order, and the l sum is a fixed shuffle tree, so results do not depend on
 // timing.
-constexpr int kMaxSplits = 64;
 constexpr int kMergeParts = 4;   // value-dim quarters per (query, head)
 constexpr int kMergeGroups = 4;  // split groups per workgroup
 constexpr int kMergeCols = kDv / kMergeParts / 4;  // float4 columns per quarter
@@ -933,18 +932,6 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void attn_merge_kernel(A
 }
 
 }  // namespace
-
-int attn_splits(int n_q_call) {
-  if (n_q_call >= 512 || n_q_call <= 0) return 1;  // an empty call has nothing to split
-  const int s = (1024 + n_q_call - 1) / n_q_call;
-  return s < kMaxSplits ? s : kMaxSplits;
-}
-
-size_t attn_partial_bytes(int rows, int splits) {
-  if (splits <= 1) return 0;
-  const size_t items = (size_t)rows * splits;
-  return items * kHeads * kDv * sizeof(float) + items * kHeads * 2 * sizeof(float);
-}
 
 hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
   if (a_in.n_q <= 0) return hipSuccess;

@@ -19,6 +19,7 @@ constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxComp = 32768;
+constexpr int kMaxSplits = 64;  // key splits per query of a small call
 
 struct IndexerArgs {
   const int8_t* iq;   // [n_q][4][64]

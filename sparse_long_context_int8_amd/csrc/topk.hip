@@ -514,59 +514,11 @@ constexpr int kFinishBlock = 512;
 constexpr int kFinishPer = 8;  // candidates a finish workgroup holds: 4096
 constexpr int kRedoGrid = 128;  // workgroups that share the recompute list
 
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.n_q <= 0) return hipSuccess;
   return launch_by_size<kDense>(a.n_comp, a, FusedArgs{}, a.n_q, stream);
-}
-
-// The fused selection serves a launch of at least 256 tokens (fewer leave
-// its passes latency-bound, and their score band is small) when every token
-// keeps at most 2048 of more than 4096 visible rows and sees at least 8 rows
-// per kept row, so that the 1-in-8 sample (16-row blocks) holds enough rows above the
-// threshold.
-bool fused_applies(int n_q, int q_pos0, int n_comp, int ratio, int top_k) {
-  if (n_q < 256 || top_k > 2048) return false;
-  const int nv_min = min(n_comp, (q_pos0 + 1) / ratio);
-  return nv_min > 4096 && nv_min >= 8 * top_k;
-}
-
-FusedPlan fused_plan(int n_comp, int top_k) {
-  FusedPlan p;
-  p.span = 512;
-  p.n_spans = (n_comp + p.span - 1) / p.span;  // <= 64 <= finish block
-  p.cap = p.span / 4;                         // about 2.5x the expected count
-  p.stride = 8;
-  // The sample holds about k/8 rows above the k-th score; asking for four
-  // standard deviations more makes a threshold below it very likely.
-  const int base = (top_k + p.stride - 1) / p.stride;
-  int sd = 1;
-  while (sd * sd < base) ++sd;
-  p.rank = base + 4 * sd + 16;
-  return p;
-}
-
-size_t fused_workspace_bytes(int n_q, const FusedPlan& p) {
-  const size_t nq = (size_t)n_q;
-  return align256(nq * 4) + align256(4) + align256(nq * 4) + align256(nq * p.n_spans * 4) +
-         align256(nq * p.n_spans * p.cap * 8);
-}
-
-void fused_bind_workspace(FusedArgs& a, void* ws) {
-  char* w = static_cast<char*>(ws);
-  const size_t nq = (size_t)a.n_q;
-  a.thresh = reinterpret_cast<int32_t*>(w);
-  w += align256(nq * 4);
-  a.n_redo = reinterpret_cast<int32_t*>(w);
-  w += align256(4);
-  a.redo_list = reinterpret_cast<int32_t*>(w);
-  w += align256(nq * 4);
-  a.counts = reinterpret_cast<int32_t*>(w);
-  w += align256(nq * a.plan.n_spans * 4);
-  a.cand = reinterpret_cast<int32_t*>(w);
 }
 
 hipError_t launch_fused_topk(const FusedArgs& f, hipStream_t stream) {
