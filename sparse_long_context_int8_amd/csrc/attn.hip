@@ -843,11 +843,41 @@ void attn_kernel(AttnArgs a) {
   }
   if (!q_valid) return;  // the pair's missing second query
   const float inv = 1.0f / l_tot;
-  float* orow = a.out + ((int64_t)r * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
+  if constexpr (GROUP == 1) {
+    // The query's output (16 heads x 512 fp32, 32 KB contiguous) goes out as
+    // whole 1 KB pieces: each wave first puts its O^T slice into LDS as
+    // [head][512] rows (16-byte unit u of head h at u ^ (h & 15), so that
+    // both the writes and the row reads below are conflict-free), then
+    // writes 8 KB (4 heads) with one contiguous 1 KB store per instruction.
+    // The chunk buffers are free here: every wave has passed the last
+    // chunk's exchange barrier, after which no wave reads them.
+    static_assert(NBUF * C::kBuf >= kHeads * kDv * 4, "output staging fits the chunk buffers");
+    static_assert((kHeads * kDv * 4) % (WAVES * 1024) == 0, "whole 1 KB pieces per wave");
 #pragma unroll
-  for (int nt = 0; nt < C::kNt; ++nt) {
-    const float4v v = acc_o[nt] * inv;
-    __builtin_nontemporal_store(v, reinterpret_cast<float4v*>(orow + 16 * nt));
+    for (int nt = 0; nt < C::kNt; ++nt) {
+      const int u = (kDv / WAVES / 4) * wave + 4 * nt + g;
+      *reinterpret_cast<__attribute__((address_space(3))) float4v*>(bufs + c16 * (kDv * 4) + ((u ^ c16) << 4)) =
+          acc_o[nt] * inv;
+    }
+    lds_barrier();
+    float4v* const orow = reinterpret_cast<float4v*>(a.out + (int64_t)r * kHeads * kDv);
+    constexpr int kPieces = (kHeads * kDv * 4) / (WAVES * 1024);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int piece = kPieces * wave + j;  // 1 KB piece of the query's output
+      const int h = piece / (kDv * 4 / 1024);
+      const int u = (piece % (kDv * 4 / 1024)) * 64 + lane;
+      const float4v v = *reinterpret_cast<const __attribute__((address_space(3))) float4v*>(
+          bufs + h * (kDv * 4) + ((u ^ h) << 4));
+      __builtin_nontemporal_store(v, orow + 64 * piece + lane);
+    }
+  } else {
+    float* orow = a.out + ((int64_t)r * kHeads + c16) * kDv + (kDv / WAVES) * wave + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < C::kNt; ++nt) {
+      const float4v v = acc_o[nt] * inv;
+      __builtin_nontemporal_store(v, reinterpret_cast<float4v*>(orow + 16 * nt));
+    }
   }
   if (a.lse && wave == 0 && g == 0) {
     a.lse[(int64_t)r * kHeads + c16] = (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
