@@ -2,14 +2,20 @@
 
 One step = one spmla_prefill call over the 8,192-token prefill workload
 (four 2,048-query bands: the selection of all four, then streaming attention
-band by band), inputs resident in HBM. The default 100 warm-up steps (about
-50 ms of GPU work) bring the GPU to its sustained clocks before the timed
-steps; after 5 warm-up steps a step still runs about 11% slower. Prints one
-JSON line:
+band by band), inputs resident in HBM. Prints one JSON line:
   value      whole-job tokens/s over the timed steps
-  roofline   the attention kernel (dominant) against the HBM roofline, with
-             algorithmic bytes per launch and its live launch duration
+  roofline   the attention kernel (dominant): algorithmic bytes per launch
+             over its live launch duration, against the measured ceiling of
+             its data movement (a kernel that moves the same bytes and
+             computes nothing, timed in the same run); the HBM-only model,
+             counter-measured DRAM traffic and matrix-core busy alongside
+  workloads  the other configurations (9,133 and 10,240 tokens, the
+             8,192-token chunk after 114,687 tokens, decode and verify
+             lanes), timed with the same steps and warm-up
   cpu_baseline  the CPU oracle timed on the host cores on a bounded sample
+
+The default 100 warm-up steps bring the GPU to its sustained clocks before
+the timed steps; after only 5 warm-up steps a step runs about 11% slower.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -28,6 +34,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix
+# L2 -> compute-unit fill rate from unit counts and clock: 256 CUs x 64 B per
+# clock x 2.4 GHz (context for the measured ceiling, not a published figure).
+L2_PEAK_DERIVED_GBS = 256 * 64 * 2.4
+# Configurations timed after the headline one, with the same steps and warm-up.
+EXTRA_WORKLOADS = ["prefill-9133", "prefill-10240", "chunk-8192-after-114687", "decode-1-at-122878",
+                   "verify-5-at-122874"]
 METRIC = "sparse-MLA prefill tokens/s per layer; % of HBM/MFMA roofline"
 # spmla_prefill hands the attention each selection in ascending row order when
 # the compressed rows (576 fp16 each) exceed one die's L2.
@@ -94,18 +106,55 @@ def src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", f"attn_kernel-{workload_name}-hbm-traffic.md")
+def attn_counters(workload_name):
+    """Counter figures of the attention launch from the committed rocprofv3
+    summary: HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) and
+    the matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the busy
+    cycles of every SIMD). Each is None if there is no summary or attn.hip
+    changed since it was taken."""
+    res = {"traffic": None, "mfma_busy": None}
+    path = os.path.join(ROOT, "profiles", f"attn_kernel-{workload_name}-counters.md")
     if not os.path.exists(path):
-        return None
+        return res
     text = open(path).read()
     m_hash = re.search(r"attn\.hip sha256\[:16\]:\s*([0-9a-f]{16})", text)
+    if not m_hash or m_hash.group(1) != src_hash(ATTN_SRC):
+        return res
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != src_hash(ATTN_SRC):
-        return None
-    return float(m_bytes.group(1))
+    m_busy = re.search(r"mfma_busy_frac:\s*([0-9.eE+]+)", text)
+    if m_bytes:
+        res["traffic"] = float(m_bytes.group(1))
+    if m_busy:
+        res["mfma_busy"] = float(m_busy.group(1))
+    return res
+
+
+def load_ceiling():
+    """libspmla_ceiling.so: the kernel that moves the attention's bytes and
+    computes nothing (its measured rate is the roofline's ceiling)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "sparse_long_context_int8_amd", "libspmla_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int32
+    lib.spmla_ceiling_gather.restype = ctypes.c_int
+    lib.spmla_ceiling_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    return lib
+
+
+def ceiling_call(lib, torch, w, dev, a0, bn, sel, out, lse, nbuf):
+    import ctypes
+
+    rc = lib.spmla_ceiling_gather(
+        ctypes.c_void_p(dev["q"][a0:a0 + bn].data_ptr()), ctypes.c_void_p(dev["kv_comp"].data_ptr()),
+        ctypes.c_void_p(dev["kv_raw"].data_ptr()), ctypes.c_void_p(sel.data_ptr()),
+        ctypes.c_void_p(out[a0:a0 + bn].data_ptr()), ctypes.c_void_p(lse[a0:a0 + bn].data_ptr()),
+        bn, w.q_pos0 + a0, w.n_comp, w.ratio, w.window, w.top_k, nbuf,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"spmla_ceiling_gather returned {rc}")
 
 
 def cpu_baseline(w, x):
@@ -237,6 +286,46 @@ def bench_attn_grouped(args, sp, workloads, torch):
     }), flush=True)
 
 
+def time_prefill(sp, torch, workloads, w, steps, warmup):
+    """Times `steps` spmla_prefill calls of workload w after `warmup` untimed
+    ones: HIP events on the launch stream around each step, inputs,
+    outputs and workspace resident on the device."""
+    log(f"workload {w.name}: generating inputs")
+    x = workloads.generate(w)
+    dev = {k: torch.from_numpy(v).cuda() for k, v in x.items()}
+    desc = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
+    out = torch.empty((w.n_q, w.n_heads, w.d_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.n_q, w.n_heads), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.n_q, w.top_k), dtype=torch.int32, device="cuda")
+    ws_bytes = sp.spmla_prefill_workspace_bytes(desc)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sp.spmla_prefill(desc, dev["q"], dev["kv_comp"], dev["kv_raw"], dev["iq"], dev["iw"],
+                         dev["ik"], out, lse, sel, ws, ws_bytes)
+
+    log(f"{w.name}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"{w.name}: timing {steps} steps")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    ms_per_step = total_ms / steps
+    return {"x": x, "dev": dev, "desc": desc, "out": out, "lse": lse, "sel": sel, "per_step": per_step,
+            "wall": wall, "ms_per_step": ms_per_step, "value": w.n_q * steps / (total_ms / 1e3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +333,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill-8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--op", choices=["prefill", "compress", "attn-grouped"], default="prefill",
@@ -284,39 +374,9 @@ def main():
         bench_attn_grouped(args, sp, workloads, torch)
         return
     w = workloads.BY_NAME[args.workload]
-    log(f"workload {w.name}: generating inputs")
-    x = workloads.generate(w)
-    dev = {k: torch.from_numpy(v).cuda() for k, v in x.items()}
-    desc = sp.make_desc(w.n_q, w.q_pos0, w.window, w.top_k, ratio=w.ratio, band=w.band)
-    out = torch.empty((w.n_q, w.n_heads, w.d_v), dtype=torch.float32, device="cuda")
-    lse = torch.empty((w.n_q, w.n_heads), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.n_q, w.top_k), dtype=torch.int32, device="cuda")
-    ws_bytes = sp.spmla_prefill_workspace_bytes(desc)
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda")
-
-    def step():
-        sp.spmla_prefill(desc, dev["q"], dev["kv_comp"], dev["kv_raw"], dev["iq"], dev["iw"],
-                         dev["ik"], out, lse, sel, ws, ws_bytes)
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    log(f"timing {args.steps} steps")
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record()
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    total_ms = evs[0].elapsed_time(evs[-1])
-    ms_per_step = total_ms / args.steps
-    value = w.n_q * args.steps / (total_ms / 1e3)
+    t = time_prefill(sp, torch, workloads, w, args.steps, args.warmup)
+    x, dev, desc, out, lse, sel = t["x"], t["dev"], t["desc"], t["out"], t["lse"], t["sel"]
+    per_step, wall, ms_per_step, value = t["per_step"], t["wall"], t["ms_per_step"], t["value"]
 
     # Per-kernel launch durations, same launch configuration (one band per
     # launch) on the same stream, HIP events between the launches. The
@@ -326,49 +386,88 @@ def main():
     ascending = w.n_comp * w.d_qk * 2 > ASCENDING_ROWS_ABOVE_BYTES
     n_bands = sp.spmla_num_bands(desc)
     scores_b = torch.empty((min(w.band, w.n_q), w.n_comp), dtype=torch.int32, device="cuda")
-    ev = {k: [] for k in ("indexer", "topk", "attn")}
     reps = max(3, args.steps // 2)
+    # sel holds the timed steps' selections; the attention gets them in the
+    # order spmla_prefill hands them over (prepared outside the timing).
+    attn_sels = [attn_order(torch, sel[b * w.band:min(w.n_q, (b + 1) * w.band)], ascending)
+                 for b in range(n_bands)]
+    launches = []
     for _ in range(reps):
         for b in range(n_bands):
             a0 = b * w.band
             bn = min(w.band, w.n_q - a0)
             d = sp.make_desc(bn, w.q_pos0 + a0, w.window, w.top_k, ratio=w.ratio, band=w.band,
                              n_raw=w.n_raw)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record()
             sp.spmla_indexer_scores(d, dev["iq"][a0:a0 + bn], dev["iw"][a0:a0 + bn], dev["ik"],
                                     scores_b[:bn])
             e[1].record()
             sp.spmla_topk(d, scores_b[:bn], sel[a0:a0 + bn])
             e[2].record()
-            attn_sel = attn_order(torch, sel[a0:a0 + bn], ascending)  # untimed preparation
-            e[3].record()
             sp.spmla_sparse_attn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"],
-                                 attn_sel, out[a0:a0 + bn], lse[a0:a0 + bn])
-            e[4].record()
-            ev["indexer"].append(e)
+                                 attn_sels[b], out[a0:a0 + bn], lse[a0:a0 + bn])
+            e[3].record()
+            launches.append(e)
     torch.cuda.synchronize()
-    launches = ev["indexer"]
     t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in launches]))
     t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in launches]))
-    t_attn = float(np.mean([e[3].elapsed_time(e[4]) for e in launches]))
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in launches]))
+
+    # The measured ceiling: the same bands through the kernel that moves the
+    # attention's bytes and computes nothing (best of 2-4 chunks in flight),
+    # timed the same way on the same stream.
+    log("data-movement ceiling")
+    ceil_lib = load_ceiling()
+    t_ceil_by_nbuf = {}
+    for nbuf in (2, 3, 4):
+        evs_c = []
+        for rep in range(2 + reps):
+            for b in range(n_bands):
+                a0 = b * w.band
+                bn = min(w.band, w.n_q - a0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ceiling_call(ceil_lib, torch, w, dev, a0, bn, attn_sels[b], out, lse, nbuf)
+                e1.record()
+                if rep >= 2:
+                    evs_c.append((e0, e1))
+        torch.cuda.synchronize()
+        t_ceil_by_nbuf[nbuf] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs_c]))
+    best_nbuf = min(t_ceil_by_nbuf, key=t_ceil_by_nbuf.get)
+    t_ceil = t_ceil_by_nbuf[best_nbuf]
 
     bytes_q = attn_bytes_per_query(w)
     flops_q = attn_flops_per_query(w)
     attn_bytes_per_launch = float(bytes_q.sum()) / n_bands
     attn_flops_per_launch = float(flops_q.sum()) / n_bands
     achieved = attn_bytes_per_launch / (t_attn / 1e3) / 1e9  # GB/s
-    traffic = measured_traffic(w.name)
+    ceiling = attn_bytes_per_launch / (t_ceil / 1e3) / 1e9  # GB/s, same bytes
+    ctr = attn_counters(w.name)
+    traffic = ctr["traffic"]
     roofline = {
-        "bound": "hbm",
+        "bound": "l2",
         "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
+        "peak": round(ceiling, 1),
         "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "frac": round(achieved / ceiling, 4),
         "traffic": traffic,
         "kernel": "attn_kernel",
+        "peak_kind": ("measured: the same bands through a kernel that moves exactly the attention's bytes "
+                      "(query rows, indices, gathered rows into LDS, outputs) and computes nothing, "
+                      f"best of 2-4 chunks of loads in flight ({best_nbuf}); the rows are L2/MALL-resident"),
+        "ceiling_ms_by_chunks_in_flight": {str(k): round(v, 4) for k, v in t_ceil_by_nbuf.items()},
+        "l2_peak_derived_gbs": L2_PEAK_DERIVED_GBS,
+        "frac_of_l2_peak_derived": round(achieved / L2_PEAK_DERIVED_GBS, 4),
         "bytes_per_launch": attn_bytes_per_launch,
         "launch_ms": round(t_attn, 4),
+        "ceiling_launch_ms": round(t_ceil, 4),
+        "hbm_model": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                      "frac": round(achieved / HBM_PEAK_GBS, 4),
+                      "note": "charges every gathered row to HBM; above 1 because the rows are cache-resident"},
+        "dram_gbs": round(traffic / (t_attn / 1e3) / 1e9, 1) if traffic else None,
+        "dram_frac": round(traffic / (t_attn / 1e3) / 1e9 / HBM_PEAK_GBS, 4) if traffic else None,
+        "mfma_busy": ctr["mfma_busy"],
         "mfma_f16_tflops": round(attn_flops_per_launch / (t_attn / 1e3) / 1e12, 1),
         "mfma_f16_frac": round(attn_flops_per_launch / (t_attn / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
     }
@@ -413,8 +512,29 @@ def main():
         "prefill_selection_ms_per_band": (round(ms_per_step / n_bands - t_attn, 4) if w.n_q >= 512 else None),
         "roofline": roofline,
         "step_roofline": step_roofline(w, ms_per_step),
+        "workloads": {},
         "cpu_baseline": None,
     }
+    if not args.no_extra:
+        # The other configurations, each a whole spmla_prefill per step with
+        # the same steps and warm-up (the headline's tensors are released
+        # first).
+        del t, dev, out, lse, sel, scores_b, attn_sels
+        torch.cuda.empty_cache()
+        for name in EXTRA_WORKLOADS:
+            if name == w.name:
+                continue
+            we = workloads.BY_NAME[name]
+            te = time_prefill(sp, torch, workloads, we, args.steps, args.warmup)
+            res["workloads"][name] = {
+                "n_q": we.n_q, "q_pos0": we.q_pos0, "top_k": we.top_k, "bands": sp.spmla_num_bands(te["desc"]),
+                "ms_per_step": round(te["ms_per_step"], 4),
+                "step_ms_median": round(float(np.median(te["per_step"])), 4),
+                "tokens_per_s": round(te["value"], 1),
+                "step_roofline": step_roofline(we, te["ms_per_step"]),
+            }
+            del te
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, x)
