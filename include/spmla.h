@@ -229,8 +229,27 @@ int spmla_compress(const spmla_desc* desc, const uint16_t* kv_raw, uint16_t* kv_
 int spmla_prefill_workspace_bytes(const spmla_desc* desc, size_t* bytes);
 
 /*
- * Steps 1-4 for all n_q queries in bands of `band` queries, all enqueued on
- * `stream` with no host round trip. Attention runs band by band. Selection
+ * Steps 1-4 for all n_q queries in bands of `band` queries (page "perf(ds4):
+ * extend sparse prefill scheduling to 10K": Summary, five independent 2,048-
+ * token bands admit one 10,240-token frontier; Production workflow, the
+ * 9,133-token prompt runs as one step of 4 full bands + a ragged 941-query
+ * band; Memory and execution shape, visibility derived, no mask stored),
+ * all enqueued on `stream` with no host round trip.
+ *
+ *   q, kv_comp, kv_raw, iq, iw, ik   as in spmla_indexer_scores and
+ *                                    spmla_sparse_attn (read only)
+ *   out      fp32  [n_q][n_heads][d_v]      (output)
+ *   lse      fp32  [n_q][n_heads]           (output, may be NULL)
+ *   sel_out  int32 [n_q][top_k]             (output, may be NULL; as
+ *                                            spmla_topk writes it)
+ *   workspace, workspace_bytes   caller-owned device scratch of at least
+ *            spmla_prefill_workspace_bytes(desc) bytes, 16-byte aligned;
+ *            its contents on entry do not matter and are garbage on return
+ *            (SPMLA_EWORKSPACE, nothing enqueued, when too small).
+ * The workspace must not be used by other work on any stream until this
+ * call's work on `stream` completes. Errors as for every entry point.
+ *
+ * Attention runs band by band. Selection
  * runs once per selection group, before the group's first attention launch:
  * through the score matrix (one indexer and one top-k launch for all of the
  * group's queries), or, for bands of at least 256 queries that each see
