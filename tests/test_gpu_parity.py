@@ -589,6 +589,50 @@ def test_fused_selection_recompute_paths(sp, case):
     assert_close(lse.cpu().numpy(), ref["lse"], f"fused {case} lse")
 
 
+FEW_LONG = [
+    # (case, n_q, q_pos0, top_k): a few tokens, each over 6,000-32,500 visible rows.
+    ("ties", 5, 24000, 2048),
+    ("all-equal", 3, 100000, 2048),
+    ("full-int8-range", 17, 60000, 512),
+    ("slice-boundary", 60, 32740, 4096),
+    ("top-1", 2, 130000, 1),
+]
+
+
+@pytest.mark.parametrize("case,n_q,q_pos0,top_k", FEW_LONG, ids=[c[0] for c in FEW_LONG])
+def test_few_tokens_long_history(sp, case, n_q, q_pos0, top_k):
+    """spmla_prefill for a few tokens over long histories (score-band
+    selection, key-split attention, ascending-row handoff): many equal
+    scores (ties broken by row), all scores equal, scores over the whole
+    int8 input range with negative weights, tokens whose visible rows end
+    on either side of 8,192, and top-k 1. Selections bit-exact, outputs
+    within tolerance."""
+    import torch
+
+    w = workloads.LayerShape(f"few-{case}", n_q=n_q, q_pos0=q_pos0, window=64, top_k=top_k)
+    say(f"[parity few long-history tokens] {case}: n_q={n_q} q_pos0={q_pos0} top_k={top_k} n_comp={w.n_comp}")
+    x = workloads.generate(w, seed=61)
+    rng = np.random.default_rng(62)
+    if case == "ties":
+        x["iq"] = rng.integers(0, 2, x["iq"].shape).astype(np.int8)
+        x["ik"] = rng.integers(0, 2, x["ik"].shape).astype(np.int8)
+        x["iw"][:] = 1
+    elif case == "all-equal":
+        x["iq"][:] = 0
+    elif case == "full-int8-range":
+        x["iq"] = rng.integers(-128, 128, x["iq"].shape).astype(np.int8)
+        x["ik"] = rng.integers(-128, 128, x["ik"].shape).astype(np.int8)
+        x["iw"] = rng.integers(-128, 128, x["iw"].shape).astype(np.int8)
+    dev = to_dev(x)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"few {case} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"few {case} lse")
+
+
 FULL_RANGE = [
     ("dense", workloads.LayerShape("int8-dense", n_q=300, q_pos0=2000, window=32, top_k=128), 31),
     ("fused", workloads.LayerShape("int8-fused", n_q=256, q_pos0=20000, window=16, top_k=512), 32),
