@@ -286,10 +286,9 @@ def bench_attn_grouped(args, sp, workloads, torch):
     }), flush=True)
 
 
-def time_prefill(sp, torch, workloads, w, steps, warmup):
-    """Times `steps` spmla_prefill calls of workload w after `warmup` untimed
-    ones: HIP events on the launch stream around each step, inputs,
-    outputs and workspace resident on the device."""
+def prepare_prefill(sp, torch, workloads, w):
+    """Inputs, outputs and workspace of workload w resident on the device,
+    and one spmla_prefill step over them."""
     log(f"workload {w.name}: generating inputs")
     x = workloads.generate(w)
     dev = {k: torch.from_numpy(v).cuda() for k, v in x.items()}
@@ -304,6 +303,13 @@ def time_prefill(sp, torch, workloads, w, steps, warmup):
         sp.spmla_prefill(desc, dev["q"], dev["kv_comp"], dev["kv_raw"], dev["iq"], dev["iw"],
                          dev["ik"], out, lse, sel, ws, ws_bytes)
 
+    return {"x": x, "dev": dev, "desc": desc, "out": out, "lse": lse, "sel": sel, "ws": ws, "step": step}
+
+
+def time_steps(torch, w, prep, steps, warmup):
+    """`warmup` untimed spmla_prefill steps, then `steps` timed ones: HIP
+    events on the launch stream around each step."""
+    step = prep["step"]
     log(f"{w.name}: warmup {warmup}")
     for _ in range(warmup):
         step()
@@ -321,9 +327,8 @@ def time_prefill(sp, torch, workloads, w, steps, warmup):
     wall = time.perf_counter() - t0
     per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     total_ms = evs[0].elapsed_time(evs[-1])
-    ms_per_step = total_ms / steps
-    return {"x": x, "dev": dev, "desc": desc, "out": out, "lse": lse, "sel": sel, "per_step": per_step,
-            "wall": wall, "ms_per_step": ms_per_step, "value": w.n_q * steps / (total_ms / 1e3)}
+    return {"per_step": per_step, "wall": wall, "ms_per_step": total_ms / steps,
+            "value": w.n_q * steps / (total_ms / 1e3)}
 
 
 def main():
@@ -374,25 +379,45 @@ def main():
         bench_attn_grouped(args, sp, workloads, torch)
         return
     w = workloads.BY_NAME[args.workload]
-    t = time_prefill(sp, torch, workloads, w, args.steps, args.warmup)
+    t = prepare_prefill(sp, torch, workloads, w)
+    # The other configurations' inputs are generated and made resident up
+    # front, so that their timed steps follow each other with no host-side
+    # generation (and an idling GPU) in between.
+    extras = {} if args.no_extra else {
+        name: prepare_prefill(sp, torch, workloads, workloads.BY_NAME[name])
+        for name in EXTRA_WORKLOADS if name != w.name}
     x, dev, desc, out, lse, sel = t["x"], t["dev"], t["desc"], t["out"], t["lse"], t["sel"]
-    per_step, wall, ms_per_step, value = t["per_step"], t["wall"], t["ms_per_step"], t["value"]
+    # One step for the selections the per-kernel measurements below use.
+    t["step"]()
+    torch.cuda.synchronize()
 
+    # The per-kernel breakdown and the data-movement ceiling run before the
+    # timed steps (they are measurements of their own, each timed with HIP
+    # events); the timed steps then start on a GPU already at its sustained
+    # clocks, also when only a few warm-up steps are asked for.
+    #
     # Per-kernel launch durations, same launch configuration (one band per
     # launch) on the same stream, HIP events between the launches. The
     # attention gets its selection in the order spmla_prefill hands it over:
     # ascending rows once the compressed rows outgrow one die's L2.
-    log("per-kernel breakdown")
+    log("per-kernel breakdown and data-movement ceiling")
     ascending = w.n_comp * w.d_qk * 2 > ASCENDING_ROWS_ABOVE_BYTES
     n_bands = sp.spmla_num_bands(desc)
     scores_b = torch.empty((min(w.band, w.n_q), w.n_comp), dtype=torch.int32, device="cuda")
-    reps = max(3, args.steps // 2)
-    # sel holds the timed steps' selections; the attention gets them in the
+    warm_reps, reps = 4, 20
+    # sel holds the first step's selections; the attention gets them in the
     # order spmla_prefill hands them over (prepared outside the timing).
     attn_sels = [attn_order(torch, sel[b * w.band:min(w.n_q, (b + 1) * w.band)], ascending)
                  for b in range(n_bands)]
+    # The measured ceiling: the same bands through the kernel that moves the
+    # attention's bytes and computes nothing, at 2, 3 and 4 chunks of loads
+    # in flight (the best counts). Each band's ceiling launches follow its
+    # attention launch in the same repetition, so both see the same clocks;
+    # the first warm_reps repetitions are not counted.
+    ceil_lib = load_ceiling()
     launches = []
-    for _ in range(reps):
+    evs_c = {nbuf: [] for nbuf in (2, 3, 4)}
+    for rep in range(warm_reps + reps):
         for b in range(n_bands):
             a0 = b * w.band
             bn = min(w.band, w.n_q - a0)
@@ -408,34 +433,25 @@ def main():
             sp.spmla_sparse_attn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"],
                                  attn_sels[b], out[a0:a0 + bn], lse[a0:a0 + bn])
             e[3].record()
-            launches.append(e)
-    torch.cuda.synchronize()
-    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in launches]))
-    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in launches]))
-    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in launches]))
-
-    # The measured ceiling: the same bands through the kernel that moves the
-    # attention's bytes and computes nothing (best of 2-4 chunks in flight),
-    # timed the same way on the same stream.
-    log("data-movement ceiling")
-    ceil_lib = load_ceiling()
-    t_ceil_by_nbuf = {}
-    for nbuf in (2, 3, 4):
-        evs_c = []
-        for rep in range(2 + reps):
-            for b in range(n_bands):
-                a0 = b * w.band
-                bn = min(w.band, w.n_q - a0)
+            if rep >= warm_reps:
+                launches.append(e)
+            for nbuf in (2, 3, 4):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 ceiling_call(ceil_lib, torch, w, dev, a0, bn, attn_sels[b], out, lse, nbuf)
                 e1.record()
-                if rep >= 2:
-                    evs_c.append((e0, e1))
-        torch.cuda.synchronize()
-        t_ceil_by_nbuf[nbuf] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs_c]))
+                if rep >= warm_reps:
+                    evs_c[nbuf].append((e0, e1))
+    torch.cuda.synchronize()
+    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in launches]))
+    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in launches]))
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in launches]))
+    t_ceil_by_nbuf = {nbuf: float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) for nbuf, ev in evs_c.items()}
     best_nbuf = min(t_ceil_by_nbuf, key=t_ceil_by_nbuf.get)
     t_ceil = t_ceil_by_nbuf[best_nbuf]
+
+    t.update(time_steps(torch, w, t, args.steps, args.warmup))
+    per_step, wall, ms_per_step, value = t["per_step"], t["wall"], t["ms_per_step"], t["value"]
 
     bytes_q = attn_bytes_per_query(w)
     flops_q = attn_flops_per_query(w)
@@ -515,17 +531,12 @@ def main():
         "workloads": {},
         "cpu_baseline": None,
     }
-    if not args.no_extra:
+    if extras:
         # The other configurations, each a whole spmla_prefill per step with
-        # the same steps and warm-up (the headline's tensors are released
-        # first).
-        del t, dev, out, lse, sel, scores_b, attn_sels
-        torch.cuda.empty_cache()
-        for name in EXTRA_WORKLOADS:
-            if name == w.name:
-                continue
+        # the same steps and warm-up, right after the headline's.
+        for name, te in extras.items():
             we = workloads.BY_NAME[name]
-            te = time_prefill(sp, torch, workloads, we, args.steps, args.warmup)
+            te.update(time_steps(torch, we, te, args.steps, args.warmup))
             res["workloads"][name] = {
                 "n_q": we.n_q, "q_pos0": we.q_pos0, "top_k": we.top_k, "bands": sp.spmla_num_bands(te["desc"]),
                 "ms_per_step": round(te["ms_per_step"], 4),
@@ -533,8 +544,6 @@ def main():
                 "tokens_per_s": round(te["value"], 1),
                 "step_roofline": step_roofline(we, te["ms_per_step"]),
             }
-            del te
-            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, x)
