@@ -16,9 +16,11 @@
 //      atomic contention low for bell-shaped score distributions);
 //   2. refinement: MSD radix select over the remaining key bits, only for
 //      the rows in that bin (usually a handful);
-//   3. ordering: the collected keys are bucketed by the top 11 bits of their
-//      offset, bucket offsets come from one prefix scan, and each key's
-//      place inside its bucket is the number of larger keys in the bucket
+//   3. ordering: the keys at or above the threshold are counted per bucket
+//      (the top 11 bits of their offset), bucket offsets come from one
+//      prefix scan, every key is scattered from registers into its bucket,
+//      and each key's place inside its bucket is the number of larger keys
+//      in the bucket
 //      (buckets hold a few keys for spread-out scores); the first k places
 //      are the output.
 // The refinement (2) runs only while the keys at or above the threshold
@@ -35,8 +37,8 @@ typedef unsigned long long u64;
 constexpr int kBins1 = 2048;  // coarse-pass and ordering bins (11 bits)
 constexpr int kBits1 = 11;
 // Elements beyond k a workgroup may collect and order. With top_k 512 over
-// at most 2,048 rows a workgroup then holds 8,256 + 12,032 B of LDS, under
-// 20 KiB, so eight share a CU and a 2,048-token band runs in one round.
+// at most 2,048 rows a workgroup then holds 8,256 B of static and 6,016 B of
+// dynamic LDS, so eight share a CU and a 2,048-token band runs in one round.
 constexpr int kSlack = 240;
 
 // Wave-wide scans and reductions with DPP (no LDS round trips): row_shr:n
@@ -132,8 +134,9 @@ enum Src : int {
   kRecompute = 2,  // scores recomputed from the indexer inputs (listed tokens)
 };
 
-// Selection and ordering for token r of the launch. LDS: `keys` holds twice
-// min(top_k + kSlack, BLOCK * PER) keys (collected, then their bucketed copy).
+// Selection and ordering for token r of the launch. LDS: `keys` holds
+// min(top_k + kSlack, BLOCK * PER) bucketed keys, then (for the ascending
+// copy) a bitmap of the visible rows.
 template <int BLOCK, int PER, int SRC>
 __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f, int r) {
   constexpr int NW = BLOCK / 64;
@@ -344,60 +347,57 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     }
   }
 
-  // 3. Collect the elements >= thresh (at most cap, at least nsel) into
-  // keys[0 ..): each thread's count, one block-wide prefix scan, then every
-  // thread writes its keys to consecutive slots; and count them per ordering
-  // bucket: the top 11 bits of (key - thresh); no key exceeds key_hi.
+  // 3. Bucket the elements >= thresh (at most cap, at least nsel) for
+  // ordering: count them per bucket (the top 11 bits of key - thresh; no key
+  // exceeds key_hi), turn the counts into bucket offsets, and scatter every
+  // key from registers straight into its bucket (in any order inside it: the
+  // placement below ranks a bucket's keys by value).
   const u64 key_hi = ((u64)span << ebits) | emask;
   const u64 kspan = key_hi - thresh;
   const int kbits = kspan ? 64 - __clzll(kspan) : 0;
   const int shb = kbits > kBits1 ? kbits - kBits1 : 0;
   __syncthreads();
   for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) mine += (i * BLOCK + tid < n_el && key_of(i) >= thresh) ? 1 : 0;
-  const int mine_incl = wave_incl_scan(mine, lane);
-  if (lane == 63) red_a[wave] = mine_incl;
   __syncthreads();
-  int pos = mine_incl - mine, n_taken = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    pos += w < wave ? red_a[w] : 0;
-    n_taken += red_a[w];
-  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (i * BLOCK + tid < n_el) {
       const u64 key = key_of(i);
-      if (key >= thresh) {
-        if (pos < cap) {  // by construction
-          keys[pos] = key;
-          atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
-        }
-        ++pos;
-      }
+      if (key >= thresh) atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
     }
   }
   __syncthreads();
-
   bucket_offsets<BLOCK>(hist, red_c);
-  const int n_coll = min(n_taken, cap);
-  u64* bucketed = keys + cap;
-  for (int e = tid; e < n_coll; e += BLOCK) {
-    const u64 key = keys[e];
-    bucketed[atomicAdd(&hist[(int)((key - thresh) >> shb)], 1)] = key;
+  u64* const bucketed = keys;
+  // Slots of up to 8 elements are claimed before any is written, so their
+  // LDS atomics are in flight together.
+  constexpr int G = PER < 8 ? PER : 8;
+#pragma unroll
+  for (int i0 = 0; i0 < PER; i0 += G) {
+    int slot[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int i = i0 + u;
+      slot[u] = -1;
+      if (i * BLOCK + tid < n_el) {
+        const u64 key = key_of(i);
+        if (key >= thresh) slot[u] = atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (slot[u] >= 0 && slot[u] < cap) bucketed[slot[u]] = key_of(i0 + u);  // < cap by construction
   }
   __syncthreads();
+  // After the scatter hist[b] is the end of bucket b; bucket 0 comes last, so
+  // hist[0] is the number of keys collected.
+  const int n_coll = min(hist[0], cap);
   // Ascending order (optional): the winners' rows are marked in a bitmap of
-  // the visible rows (nv <= kMaxComp bits) and read back in row order after
-  // a block-wide scan of the words' popcounts. The bitmap takes keys[0, cap),
-  // which is free once scattered, when it fits there (2 * cap words);
-  // otherwise it follows the bucketed copy, where the launcher reserves
-  // asc_bitmap_words(n_comp, cap) words. It never overlaps the bucketed keys,
-  // which the placement below still reads.
+  // the visible rows (nv <= kMaxComp bits), which follows the bucketed keys
+  // (the launcher reserves asc_bitmap_words(n_comp) words), and read back in
+  // row order after a block-wide scan of the words' popcounts.
   const int nwords = (nv + 31) >> 5;
-  unsigned* const bits = reinterpret_cast<unsigned*>(nwords <= 2 * cap ? keys : keys + 2 * cap);
+  unsigned* const bits = reinterpret_cast<unsigned*>(keys + cap);
   if (a.sel_asc) {
     for (int i = tid; i < nwords; i += BLOCK) bits[i] = 0u;
     __syncthreads();
@@ -474,27 +474,16 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(TopkArgs a, FusedArgs f) {
 }
 
 // Words of LDS reserved after the bucketed keys for the ascending-order
-// bitmap: none when a bitmap of every visible row (at most n_comp) fits in
-// the 2 * cap words of the collected keys, which are free by then.
-size_t asc_bitmap_words(int n_comp, int cap) {
-  const size_t words = ((size_t)n_comp + 31) / 32;
-  return words <= 2 * (size_t)cap ? 0 : words;
-}
+// bitmap: one bit per compressed row a token can see.
+size_t asc_bitmap_words(int n_comp) { return ((size_t)n_comp + 31) / 32; }
 
 template <int BLOCK, int PER, int SRC>
 hipError_t launch_cfg(const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
-  // keys: the collected elements (at most top_k + kSlack) and their bucketed
-  // copy, then the ascending-order bitmap when it does not fit over the first.
+  // keys: the bucketed elements (at most top_k + kSlack), then the
+  // ascending-order bitmap.
   const int cap = std::min(a.top_k + kSlack, BLOCK * PER);
-  size_t lds = 2 * sizeof(u64) * (size_t)cap;
-  if (a.sel_asc) {
-    const size_t extra = asc_bitmap_words(a.n_comp, cap);
-    lds += sizeof(unsigned) * extra;
-    // Every token sees at most n_comp rows: its bitmap of ceil(nv / 32)
-    // words fits wherever the kernel puts it.
-    const size_t words = ((size_t)a.n_comp + 31) / 32;
-    if (!(words <= 2 * (size_t)cap || extra >= words)) return hipErrorInvalidValue;
-  }
+  size_t lds = sizeof(u64) * (size_t)cap;
+  if (a.sel_asc) lds += sizeof(unsigned) * asc_bitmap_words(a.n_comp);
   hipLaunchKernelGGL((topk_kernel<BLOCK, PER, SRC>), dim3(grid), dim3(BLOCK), lds, stream, a, f);
   return hipGetLastError();
 }
