@@ -507,6 +507,37 @@ def test_largest_topk_long_history(sp):
     assert_close(o2.cpu().numpy(), ref["out"], f"{w.name} prefill out")
 
 
+LARGEST = [
+    # (case, n_q, q_pos0, top_k, window): n_comp = (q_pos0 + n_q) // 4 = 32,768, the largest supported.
+    ("dense-k4096", 64, 131072 - 64, 4096, 200),
+    ("fused-k2048", 256, 131072 - 256, 2048, 200),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case,n_q,q_pos0,top_k,window", LARGEST, ids=[c[0] for c in LARGEST])
+def test_largest_history(sp, case, n_q, q_pos0, top_k, window):
+    """32,768 compressed rows (the largest supported history) through
+    spmla_prefill: top-k 4,096 of a short call (score band, key-split
+    attention) and top-k 2,048 of a 256-token call (fused selection, whole
+    queries), both gathering in ascending row order. Every selection
+    bit-exact, outputs within tolerance."""
+    import torch
+
+    w = workloads.LayerShape(f"largest-{case}", n_q=n_q, q_pos0=q_pos0, window=window, top_k=top_k)
+    assert w.n_comp == 32768
+    say(f"[parity largest history] {case}: n_q={n_q} q_pos0={q_pos0} top_k={top_k} n_comp={w.n_comp}")
+    x = workloads.generate(w, seed=70)
+    dev = to_dev(x)
+    ref = oracle.prefill(x, q_pos0=w.q_pos0, ratio=w.ratio, window=w.window, top_k=w.top_k,
+                         scale=w.scale, d_v=w.d_v)
+    out, lse, sel = sp.prefill(desc_of(sp, w), dev)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref["sel"])
+    assert_close(out.cpu().numpy(), ref["out"], f"{case} out")
+    assert_close(lse.cpu().numpy(), ref["lse"], f"{case} lse")
+
+
 def random_shapes(n_small=12, n_large=4, seed=2024):
     """Seeded random descriptors: 1-300 queries (key-split attention) and
     513-900 queries (whole-query attention), positions up to 6,000, windows
