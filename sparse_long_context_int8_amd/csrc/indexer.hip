@@ -185,17 +185,20 @@ constexpr int kCodes = 2048;
 // workgroup per 4 tokens (one A tile); its 4 waves take turns over the
 // sampled rows, one block of 16 consecutive rows in every 16 * stride (whole
 // 128-byte lines of the int8 keys, where single rows every stride apart would
-// use half of each line). Each sampled
-// visible score lands in a per-token LDS histogram of score codes; the
+// use half of each line). Each workgroup starts its walk over the sampled
+// blocks at its own offset, so that the workgroups in flight read different
+// key lines at any moment instead of all queueing on the same L2 channel.
+// Each sampled visible score lands in a per-token LDS histogram of score
+// codes (16-bit counts, two per word: a token has at most 4,096 samples); the
 // threshold is the lowest score of the code bin in which the count from the
 // top reaches `rank` (INT32_MIN if fewer samples than that).
 __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
-  __shared__ int hist[4][kCodes];
+  __shared__ unsigned hist[4][kCodes / 2];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int t0 = blockIdx.x * 4;
-  for (int i = threadIdx.x; i < 4 * kCodes; i += 256) (&hist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 2 * kCodes; i += 256) (&hist[0][0])[i] = 0u;
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_redo = 0;  // the finish pass fills the list
 
   const int tok_a = t0 + (col >> 2);
@@ -209,49 +212,62 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
   const int nv_max = min(a.n_comp, (a.q_pos0 + t_last + 1) / a.ratio);
   const int stride = a.plan.stride;
   const int n_steps = (nv_max + 16 * stride - 1) / (16 * stride);
+  const int rot = n_steps > 0 ? (int)(((unsigned)blockIdx.x * 97u) % (unsigned)n_steps) : 0;
   __syncthreads();
 
   constexpr int kUnroll = 4;
   for (int s0 = wave * kUnroll; s0 < n_steps; s0 += 4 * kUnroll) {
     v4i b[kUnroll];
+    int j[kUnroll];
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
-      const int j = 16 * stride * (s0 + q) + col;
-      b[q] = (s0 + q < n_steps && j < a.n_comp)
-                 ? *reinterpret_cast<const v4i*>(a.ik + (int64_t)j * kIdxDim + grp * 16)
+      int step = s0 + q + rot;
+      if (step >= n_steps) step -= n_steps;
+      j[q] = 16 * stride * step + col;
+      b[q] = (s0 + q < n_steps && j[q] < a.n_comp)
+                 ? *reinterpret_cast<const v4i*>(a.ik + (int64_t)j[q] * kIdxDim + grp * 16)
                  : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int q = 0; q < kUnroll; ++q) {
-      const int j = 16 * stride * (s0 + q) + col;
       const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(afrag, b[q], v4i{0, 0, 0, 0}, 0, 0, 0);
-      if (s0 + q < n_steps && j < nv) atomicAdd(&hist[grp][score_code(head_sum(acc, hw))], 1);
+      if (s0 + q < n_steps && j[q] < nv) {
+        const int c = score_code(head_sum(acc, hw));
+        atomicAdd(&hist[grp][c >> 1], 1u << (16 * (c & 1)));
+      }
     }
   }
   __syncthreads();
 
   // Wave w sets the threshold of token t0 + w; lane l owns codes
-  // kCodes-1 - kPer*l down to kCodes - kPer*(l+1) (scanned from the top).
+  // kCodes-1 - kPer*l down to kCodes - kPer*(l+1) (scanned from the top),
+  // kPer / 2 words, which it sums in a rotated order so that the lanes of a
+  // read hit different LDS banks.
   constexpr int kPer = kCodes / 64;
+  constexpr int kWords = kPer / 2;
   const int tw = t0 + wave;
   if (tw >= a.n_q) return;
+  const unsigned* const hw_row = hist[wave];
+  const int w_lo = (kCodes - kPer * (lane + 1)) / 2;  // the lane's lowest word
   int tot = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) tot += hist[wave][kCodes - 1 - kPer * lane - i];
+  for (int i = 0; i < kWords; ++i) {
+    const unsigned v = hw_row[w_lo + ((i + lane) & (kWords - 1))];
+    tot += (int)(v & 0xffffu) + (int)(v >> 16);
+  }
   int incl = tot;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int u = __shfl_up(incl, o);
     if (lane >= o) incl += u;
   }
-  const int total = __shfl(incl, 63);
   const int need = a.plan.rank;
   int code = -1;
   int above = incl - tot;
   if (above < need && need <= incl) {
     for (int i = 0; i < kPer; ++i) {
       const int c = kCodes - 1 - kPer * lane - i;
-      above += hist[wave][c];
+      above += (int)((hw_row[c >> 1] >> (16 * (c & 1))) & 0xffffu);
       if (above >= need) {
         code = c;
         break;
@@ -265,7 +281,6 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
   } else if (code >= 0) {
     a.thresh[tw] = code_lo(code);
   }
-  (void)total;
 }
 
 // Collect pass: the indexer's 64-token x span tiling with exact scores; every
