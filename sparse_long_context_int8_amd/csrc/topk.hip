@@ -165,18 +165,21 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     return;
   }
 
-  // Elements of this token in registers; element e = i*BLOCK + tid, n_el of
-  // them. Dense and recomputed elements are rows 0 .. nv-1 in order;
-  // candidates carry their row.
+  // Elements of this token in registers, n_el of them; bit i of `vm` says
+  // whether register i holds one. Dense and recomputed elements are rows
+  // 0 .. nv-1 in order (element i*BLOCK + tid); candidates carry their row.
   int sc[PER];
   int jx[SRC == kCandidate ? PER : 1];
   int n_el = nv;
+  unsigned vm = 0u;
+  static_assert(PER <= 32, "validity bits");
   if constexpr (SRC == kDense) {
     const int32_t* row = a.scores + (int64_t)r * a.ld_scores;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = i * BLOCK + tid;
       sc[i] = e < nv ? __builtin_nontemporal_load(row + e) : INT32_MIN;
+      vm |= e < nv ? 1u << i : 0u;
     }
   } else if constexpr (SRC == kRecompute) {
     // S[t][j] = sum_h w[t][h] * max(0, <iq[t][h][:], ik[j][:]>), exact.
@@ -189,6 +192,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     for (int i = 0; i < PER; ++i) {
       const int e = i * BLOCK + tid;
       sc[i] = INT32_MIN;
+      vm |= e < nv ? 1u << i : 0u;
       if (e < nv) {
         const int4* krow = reinterpret_cast<const int4*>(f.ik + (int64_t)e * kIdxDim);
         int kv[16];
@@ -212,56 +216,95 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
       }
     }
   } else {
-    // Candidates: per-span slot counts -> offsets. The token goes on the
-    // recompute list if a span overflowed its slots, if fewer than nsel
-    // candidates exist (the threshold was too high), or if they do not fit
-    // this workgroup: then they are not provably a superset of the top-k.
+    // Candidates. The token goes on the recompute list if a span overflowed
+    // its slots, if fewer than nsel candidates exist (the threshold was too
+    // high), or if they do not fit this workgroup: then they are not provably
+    // a superset of the top-k. Register i of wave w holds slot `lane` of span
+    // w + NW*i: those loads go out together with the span counts (one
+    // round trip), and a slot is an element while it is below its span's
+    // count. A span with more than 64 candidates does not fit that layout;
+    // then the slots are packed by a prefix scan over the spans (a second
+    // round trip).
     const int ns = f.plan.n_spans;  // <= BLOCK (host-checked)
     const int cap = f.plan.cap;
-    const int cnt = tid < ns ? f.counts[(int64_t)r * ns + tid] : 0;
-    const int held = min(cnt, cap);
-    const int incl = wave_incl_scan(held, lane);
-    if (lane == 63) red_a[wave] = incl;
-    const unsigned long long over = __ballot(cnt > cap);
-    if (lane == 0) red_b[wave] = over ? 1 : 0;
+    static_assert(NW * PER >= (kMaxComp + 511) / 512, "one register per span and lane");
+    const int32_t* cand_row = f.cand + 2 * ((int64_t)r * ns * cap);
+    int cnt_i[PER];
+    int wtot = 0, wflags = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int sp = wave + NW * i;  // wave-uniform
+      cnt_i[i] = sp < ns ? f.counts[(int64_t)r * ns + sp] : 0;
+      sc[i] = INT32_MIN;
+      jx[i] = 0;
+      if (sp < ns && lane < cap) {
+        const int2 c = *reinterpret_cast<const int2*>(cand_row + 2 * ((int64_t)sp * cap + lane));
+        sc[i] = c.x;
+        jx[i] = c.y;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      wtot += min(cnt_i[i], cap);
+      wflags |= (cnt_i[i] > cap ? 1 : 0) | (cnt_i[i] > 64 ? 2 : 0);
+    }
+    if (lane == 0) {
+      red_a[wave] = wtot;
+      red_b[wave] = wflags;
+    }
     __syncthreads();
-    int before = 0, total = 0, any_over = 0;
+    int total = 0, flags = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      before += w < wave ? red_a[w] : 0;
       total += red_a[w];
-      any_over |= red_b[w];
+      flags |= red_b[w];
     }
-    if (tid < ns) aux[tid] = before + incl - held;
-    const bool fail = any_over || total < nsel || total > BLOCK * PER;
+    __syncthreads();  // every wave has read red_a and red_b before they are written again
+    const bool fail = (flags & 1) || total < nsel || total > BLOCK * PER;
     if (fail) {
       if (tid == 0) f.redo_list[atomicAdd(f.n_redo, 1)] = r;
       return;
     }
-    // Slots [aux[s], aux[s] + held) are span s's; label each with its span so
-    // that an element finds its span with one LDS read.
-    if (tid < ns)
-      for (int e = aux[tid], e1 = aux[tid] + held; e < e1; ++e) span_of[e] = (unsigned char)tid;
-    __syncthreads();
     n_el = total;
-    const int32_t* cand_row = f.cand + 2 * ((int64_t)r * ns * cap);
+    if (!(flags & 2)) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = i * BLOCK + tid;
-      sc[i] = INT32_MIN;
-      jx[i] = 0;
-      if (e < n_el) {
-        const int lo = span_of[e];
-        const int2 c = *reinterpret_cast<const int2*>(cand_row + 2 * ((int64_t)lo * cap + (e - aux[lo])));
-        sc[i] = c.x;
-        jx[i] = c.y;
+      for (int i = 0; i < PER; ++i) vm |= lane < min(cnt_i[i], cap) ? 1u << i : 0u;
+    } else {
+      // Packed: element e = i*BLOCK + tid; slots [aux[s], aux[s] + held)
+      // are span s's, each labelled with its span so that an element finds
+      // its span with one LDS read.
+      const int cnt = tid < ns ? f.counts[(int64_t)r * ns + tid] : 0;
+      const int held = min(cnt, cap);
+      const int incl = wave_incl_scan(held, lane);
+      if (lane == 63) red_a[wave] = incl;
+      __syncthreads();
+      int before = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) before += w < wave ? red_a[w] : 0;
+      if (tid < ns) aux[tid] = before + incl - held;
+      __syncthreads();
+      if (tid < ns)
+        for (int e = aux[tid], e1 = aux[tid] + held; e < e1; ++e) span_of[e] = (unsigned char)tid;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = i * BLOCK + tid;
+        sc[i] = INT32_MIN;
+        jx[i] = 0;
+        if (e < n_el) {
+          const int lo = span_of[e];
+          const int2 c = *reinterpret_cast<const int2*>(cand_row + 2 * ((int64_t)lo * cap + (e - aux[lo])));
+          sc[i] = c.x;
+          jx[i] = c.y;
+          vm |= 1u << i;
+        }
       }
     }
   }
   int vmax = INT32_MIN, vmin = INT32_MAX;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if (i * BLOCK + tid < n_el) {
+    if ((vm >> i) & 1u) {
       vmax = max(vmax, sc[i]);
       vmin = min(vmin, sc[i]);
     }
@@ -302,10 +345,8 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = i * BLOCK + tid;
-      if (e < n_el) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
-    }
+    for (int i = 0; i < PER; ++i)
+      if ((vm >> i) & 1u) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
     __syncthreads();
     find_bin<BLOCK>(hist, kBins1, k, &s_bin, &s_above, &s_count, red_c);
     const int bin1 = s_bin;
@@ -327,8 +368,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
         const int dbits = top - shift;  // digit width this pass (<= 8)
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-          const int e = i * BLOCK + tid;
-          if (e < n_el) {
+          if ((vm >> i) & 1u) {
             const u64 key = key_of(i);
             if ((key >> top) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << dbits) - 1)], 1);
           }
@@ -361,7 +401,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if (i * BLOCK + tid < n_el) {
+    if ((vm >> i) & 1u) {
       const u64 key = key_of(i);
       if (key >= thresh) atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
     }
@@ -379,7 +419,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
       slot[u] = -1;
-      if (i * BLOCK + tid < n_el) {
+      if ((vm >> i) & 1u) {
         const u64 key = key_of(i);
         if (key >= thresh) slot[u] = atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
       }
