@@ -97,13 +97,26 @@ __device__ __forceinline__ v4i tile_scores(const TokenTiles& tt, int m, const v4
 // VEC: 16-byte stores; the row stride is a multiple of 4 and at least n_comp
 // rounded up to 4, so a group that straddles n_comp stays inside the row
 // (its entries past n_comp are INT32_MIN).
+// Dies: workgroups are dealt to the 8 dies round-robin by their linear index.
+constexpr int kDies = 8;
+
 template <bool VEC>
 __global__ __launch_bounds__(256) void indexer_kernel(IndexerArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t_base = blockIdx.y * kQTile + wave * 16;  // first token of this wave
+  // With xcd_tiles, every span of token tile T runs on die T mod 8 (the grid
+  // has a multiple of 8 tiles): the tile's query rows are then read by the
+  // workgroups of one die, whose L2 serves all but the first.
+  int span_idx = blockIdx.x, tile = blockIdx.y;
+  if (a.xcd_tiles) {
+    const unsigned lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const unsigned q = lin / kDies;
+    tile = (int)(kDies * (q / gridDim.x) + lin % kDies);
+    span_idx = (int)(q % gridDim.x);
+  }
+  const int t_base = tile * kQTile + wave * 16;  // first token of this wave
   if (t_base >= a.n_q) return;
-  const int j_begin = blockIdx.x * a.span;
+  const int j_begin = span_idx * a.span;
   const int j_end = min(a.n_comp, j_begin + a.span);
 
   // Rows visible to the last token of this wave bound the columns to score.
@@ -365,7 +378,11 @@ hipError_t launch_indexer(const IndexerArgs& a_in, hipStream_t stream) {
   int steps_per_wg = (int)(((int64_t)col_steps * q_tiles) / 2048);
   if (steps_per_wg < 1) steps_per_wg = 1;
   a.span = steps_per_wg * kJStep;
-  dim3 grid((a.n_comp + a.span - 1) / a.span, q_tiles);
+  // Die-aligned tiles for launches of at least 16 tiles (fewer would leave
+  // padding workgroups idle for a sizeable share of the grid).
+  a.xcd_tiles = q_tiles >= 16 ? 1 : 0;
+  const int grid_tiles = a.xcd_tiles ? (q_tiles + kDies - 1) / kDies * kDies : q_tiles;
+  dim3 grid((a.n_comp + a.span - 1) / a.span, grid_tiles);
   // 16-byte groups may run past n_comp into the row padding, never past
   // the row stride.
   const int64_t n_comp4 = ((int64_t)a.n_comp + 3) / 4 * 4;

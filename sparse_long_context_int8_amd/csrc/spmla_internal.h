@@ -33,6 +33,7 @@ struct IndexerArgs {
   int32_t ratio;
   int32_t fill_invisible;  // also write INT32_MIN where no token can see the row
   int32_t span;            // compressed rows per workgroup (set by the launcher)
+  int32_t xcd_tiles;       // token tiles dealt to dies by tile mod 8 (set by the launcher)
 };
 
 struct TopkArgs {
