@@ -298,12 +298,19 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedArgs a) {
 
 // Collect pass: the indexer's 64-token x span tiling with exact scores; every
 // visible score >= the token's threshold is written as (score, row) into the
-// token's slots for this span. Slots are claimed with an LDS counter per
-// token (only the token's own wave touches it), so the order inside a span is
-// arrival order; the finish pass orders candidates exactly. The count written
-// at the end is the true count, so the finish pass can detect a full span.
+// token's slots for this span. In a 16x16 result the 16 lanes of a row hold
+// one token (4 adjacent key rows each), and only this wave sees that token,
+// so its slot counter lives in registers: per step, one inclusive scan of the
+// lanes' counts inside each 16-lane row (the four tiles' counts packed one
+// byte each: at most 64 per row) gives every lane its place, and a swizzle
+// broadcasts the row total. The step's candidates of a row are first packed
+// in the wave's LDS area, then written with one store instruction per tile
+// and 16 of them (16 consecutive slots per row): scattered single stores,
+// one instruction per tile and key row, were a quarter of the pass. Slots
+// follow (step, lane, key row) order. The count written at the end is the
+// true count, so the finish pass can detect a full span.
 __global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
-  __shared__ int claimed[kQTile];
+  __shared__ int2 stage_[4][4][4][64];  // [wave][tile m][row grp][entry]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t_base = blockIdx.y * kQTile + wave * 16;
@@ -315,8 +322,7 @@ __global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
   const int nv_wave = min(a.n_comp, (a.q_pos0 + t_last + 1) / a.ratio);
   const int col = lane & 15, grp = lane >> 4;
   const int cap = a.plan.cap;
-  int* const cnt = claimed + wave * 16;  // this wave's 16 tokens, local index 4m + grp
-  if (lane < 16) cnt[lane] = 0;
+  int2(*const stage)[4][64] = stage_[wave];
 
   TokenTiles tt;
   tt.load(a.iq, a.iw, a.n_q, a.q_pos0, a.n_comp, a.ratio, t_base, col, grp);
@@ -330,39 +336,60 @@ __global__ __launch_bounds__(256) void collect_kernel(FusedArgs a) {
     slots[m] = a.cand + 2 * (((int64_t)(ok ? tt.tok[m] : 0) * a.plan.n_spans + span_idx) * cap);
   }
 
+  int run[4] = {0, 0, 0, 0};  // slots claimed so far by the row's token in tile m
   const int j_score_end = min(j_end, nv_wave);
   for (int j0 = j_begin; j0 < j_score_end; j0 += kJStep) {
     v4i bfrag[4];
     load_b(a.ik, a.n_comp, j0, col, grp, bfrag);
     const int jl = j0 + 4 * col;
     v4i sc[4];
-    int c[4], base[4];
+    int packed = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       sc[m] = tile_scores(tt, m, bfrag);
-      c[m] = 0;
+      int c = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) c[m] += (jl + u < lim[m] && sc[m][u] >= thr[m]) ? 1 : 0;
+      for (int u = 0; u < 4; ++u) c += (jl + u < lim[m] && sc[m][u] >= thr[m]) ? 1 : 0;
+      packed |= c << (8 * m);
     }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) base[m] = c[m] ? atomicAdd(&cnt[4 * m + grp], c[m]) : 0;
+    // Inclusive scan inside each 16-lane row (row_shr 1, 2, 4, 8), then the
+    // row total from the row's lane 15 (swizzle: lane (l & 16) | 15 of each
+    // 32-lane half).
+    int incl = packed;
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);
+    const int tot = __builtin_amdgcn_ds_swizzle(incl, 0x1f0);
+    const int excl = incl - packed;
+    // Pack the row's candidates (LDS operations of one wave complete in
+    // order, so the reads below see these writes).
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      if (c[m] == 0) continue;
-      int pos = base[m];
+      int e = (excl >> (8 * m)) & 0xff;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (jl + u < lim[m] && sc[m][u] >= thr[m]) {
-          if (pos < cap) *reinterpret_cast<int2*>(slots[m] + 2 * pos) = int2{sc[m][u], jl + u};
-          ++pos;
+          stage[m][grp][e] = int2{sc[m][u], jl + u};
+          ++e;
         }
       }
+    }
+    // Entries col, col + 16, ... of each row go to consecutive slots.
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int n = (tot >> (8 * m)) & 0xff;
+      for (int e = col; e < n; e += 16) {
+        const int pos = run[m] + e;
+        if (pos < cap) *reinterpret_cast<int2*>(slots[m] + 2 * pos) = stage[m][grp][e];
+      }
+      run[m] += n;
     }
   }
   if (col == 0) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      if (tt.tok[m] < a.n_q) a.counts[(int64_t)tt.tok[m] * a.plan.n_spans + span_idx] = cnt[4 * m + grp];
+      if (tt.tok[m] < a.n_q) a.counts[(int64_t)tt.tok[m] * a.plan.n_spans + span_idx] = run[m];
   }
 }
 
