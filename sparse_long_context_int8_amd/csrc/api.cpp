@@ -189,6 +189,7 @@ spmla::AttnArgs attn_args(const spmla_desc* d, const uint16_t* q, const uint16_t
   a.splits = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  a.band_items = 0;
   return a;
 }
 
@@ -264,7 +265,20 @@ int run_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
       if (rc) return;
     }
 
-    // Attention band by band.
+    // Attention band by band: whole queries in one launch over the group's
+    // bands (each band dealt to the dies as its own launch would be, the next
+    // band starting as the previous one drains); key splits in a launch per
+    // band, whose partials share the scratch.
+    if (spmla::attn_splits(d->n_q) == 1) {
+      const int32_t* sel = ascending ? ws_sel_asc : gsel;
+      spmla::AttnArgs aa = attn_args(d, q + g0 * spmla::kHeads * spmla::kDqk, kv_comp, kv_raw, sel,
+                                     out + g0 * spmla::kHeads * spmla::kDv, lse ? lse + g0 * spmla::kHeads : nullptr);
+      aa.n_q = gn;
+      aa.q_pos0 = gpos0;
+      aa.band_items = d->band;
+      rc = hip_status(spmla::launch_attn(aa, st), "attention launch");
+      return;
+    }
     for (int64_t b0 = g0; b0 < g1; b0 += d->band) {
       const int bn = band_len(d, b0);
       const int64_t row = b0 - g0;  // first row of this band's selections within the group

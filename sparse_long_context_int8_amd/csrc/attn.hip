@@ -59,10 +59,23 @@ constexpr int kXcds = 8;             // accelerator complex dies, round-robin di
 // prefill: more visible rows) every die gets one later and one earlier slice,
 // the later one first.
 __host__ __device__ inline int attn_slice_len(int n_items) { return (n_items + 2 * kXcds - 1) / (2 * kXcds); }
-__device__ inline int attn_item(int n_items) {
+__device__ inline int attn_item_at(int idx, int n_items) {
   const int slice_len = attn_slice_len(n_items);
-  const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+  const int x = idx % kXcds, l = idx / kXcds;
   return l < slice_len ? (2 * kXcds - 1 - x) * slice_len + l : x * slice_len + (l - slice_len);
+}
+// Banded launch (AttnArgs::band_items): band b takes workgroups
+// [b * G, (b + 1) * G) with G = 2 * kXcds * slice_len(band_items), a multiple
+// of kXcds, so each band is dealt to the dies exactly as its own launch would
+// be. Returns the item, or n_items for a workgroup without one.
+__device__ inline int attn_item_banded(int n_items, int band_items) {
+  const int g = 2 * kXcds * attn_slice_len(band_items);
+  const int b = blockIdx.x / g;
+  const int first = b * band_items;
+  if (first >= n_items) return n_items;
+  const int n_band = min(band_items, n_items - first);
+  const int it = attn_item_at(blockIdx.x - b * g, n_band);
+  return it < n_band ? first + it : n_items;
 }
 
 // XOR swizzles of the 16-byte units of the LDS images, as linear maps of
@@ -274,7 +287,8 @@ void attn_kernel(AttnArgs a) {
 
   // Work items: (query r, key split s), or a query pair; see attn_item.
   const int n_items = GROUP == 1 ? a.n_q * a.splits : (a.n_q + 1) / 2;
-  const int item = attn_item(n_items);
+  const int item = GROUP == 1 && a.band_items > 0 ? attn_item_banded(n_items, a.band_items)
+                                                 : attn_item_at(blockIdx.x, n_items);
   if (item >= n_items) return;
 
   const int lane = threadIdx.x & 63;
@@ -967,7 +981,12 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
   if (a_in.n_q <= 0) return hipSuccess;
   AttnArgs a = a_in;
   if (a.splits < 1) a.splits = 1;
-  const int grid = 2 * kXcds * attn_slice_len(a.n_q * a.splits);
+  if (a.splits > 1 || a.band_items >= a.n_q) a.band_items = 0;
+  int grid = 2 * kXcds * attn_slice_len(a.n_q * a.splits);
+  if (a.band_items > 0) {
+    const int full = a.n_q / a.band_items, rest = a.n_q - full * a.band_items;
+    grid = full * 2 * kXcds * attn_slice_len(a.band_items) + (rest ? 2 * kXcds * attn_slice_len(rest) : 0);
+  }
   constexpr int W = SPMLA_ATTN_WAVES;
   hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE, 1>),
                      dim3(grid), dim3(64 * W), 0, stream, a);
@@ -982,6 +1001,7 @@ hipError_t launch_attn_grouped(const AttnArgs& a_in, hipStream_t stream) {
   if (a_in.n_q <= 0) return hipSuccess;
   AttnArgs a = a_in;
   a.splits = 1;
+  a.band_items = 0;
   const int pairs = (a.n_q + 1) / 2;
   const int grid = 2 * kXcds * attn_slice_len(pairs);
   // Bitmaps of the two queries' rows and the pair's row list.

@@ -114,6 +114,11 @@ struct AttnArgs {
   int32_t splits;
   float* part_o;            // [n_q * splits][16][512]
   float* part_ml;           // [n_q * splits][16][2]
+  // Whole queries only (splits == 1): if > 0, the launch covers its queries
+  // as consecutive bands of band_items queries (the last one ragged), each
+  // dealt to the dies as a launch of its own would be, band after band, so
+  // that a band's first queries start as the previous band's last finish.
+  int32_t band_items;
 };
 
 // Key splits per query for a call of n_q_call queries (enough work items to
