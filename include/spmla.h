@@ -164,7 +164,8 @@ int spmla_topk(const spmla_desc* desc, const int32_t* scores, int32_t* sel, int3
  *   z      = scale * <q[t][h][:], key[:]>           (all d_qk dims)
  *   out    = sum softmax(z) * key[0:d_v]            (fp32 accumulate)
  *   lse    = log(sum exp(z))                        (natural log)
- * A row of sel ends at the first -1; entries after it are not read.
+ * Entries i < min(top_k, n_vis(t)) of a sel row are read; -1 entries
+ * (padding) are skipped.
  *
  *   q        fp16  [n_q][n_heads][d_qk]
  *   kv_comp  fp16  [n_comp][d_qk]          (may be NULL if n_comp == 0)
@@ -172,8 +173,10 @@ int spmla_topk(const spmla_desc* desc, const int32_t* scores, int32_t* sel, int3
  *   sel      int32 [n_q][top_k]            (as written by spmla_topk)
  *   out      fp32  [n_q][n_heads][d_v]     (output)
  *   lse      fp32  [n_q][n_heads]          (output; may be NULL)
- * Every sel entry must be -1 or in [0, n_vis(t)); the kernel clamps an
- * out-of-range index to a valid row rather than read out of bounds.
+ * Every sel entry should be -1 or in [0, n_vis(t)); any other entry is
+ * skipped like -1 (the gather reads a valid row in its place and the key is
+ * masked out of the softmax), never dereferenced. A call over more than
+ * `band` queries is dealt to the GPU band by band in one launch.
  */
 int spmla_sparse_attn(const spmla_desc* desc, const uint16_t* q, const uint16_t* kv_comp,
                       const uint16_t* kv_raw, const int32_t* sel, float* out, float* lse,

@@ -382,7 +382,8 @@ int spmla_sparse_attn(const spmla_desc* d, const uint16_t* q, const uint16_t* kv
   REQUIRE_PTR(sel);
   REQUIRE_PTR(out);
   OPTIONAL_PTR(lse);
-  const spmla::AttnArgs a = attn_args(d, q, kv_comp, kv_raw, sel, out, lse);
+  spmla::AttnArgs a = attn_args(d, q, kv_comp, kv_raw, sel, out, lse);
+  a.band_items = d->band;  // a call over several bands is dealt to the dies band by band
   return hip_status(spmla::launch_attn(a, (hipStream_t)stream), "attention launch");
 }
 
