@@ -40,12 +40,25 @@ struct GatherArgs {
   float* out;          // [n_q][16][512], written with zeros
   float* lse;          // [n_q][16], written with zeros
   int32_t n_q, q_pos0, n_comp, ratio, window, top_k;
+  int32_t band;        // > 0: queries dealt to the dies band by band (as the attention's banded launch)
 };
 
-__device__ inline int item_of(int n_items) {
-  const int slice_len = (n_items + 2 * kXcds - 1) / (2 * kXcds);
-  const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+__host__ __device__ inline int slice_len_of(int n_items) { return (n_items + 2 * kXcds - 1) / (2 * kXcds); }
+__device__ inline int item_at(int idx, int n_items) {
+  const int slice_len = slice_len_of(n_items);
+  const int x = idx % kXcds, l = idx / kXcds;
   return l < slice_len ? (2 * kXcds - 1 - x) * slice_len + l : x * slice_len + (l - slice_len);
+}
+// Band b takes workgroups [b * G, (b + 1) * G), G = 2 * kXcds * slice_len(band),
+// dealt inside its range as a launch of that band alone.
+__device__ inline int item_of(int n_items, int band) {
+  if (band <= 0 || band >= n_items) return item_at(blockIdx.x, n_items);
+  const int g = 2 * kXcds * slice_len_of(band);
+  const int b = blockIdx.x / g, first = b * band;
+  if (first >= n_items) return n_items;
+  const int n_band = min(band, n_items - first);
+  const int it = item_at(blockIdx.x - b * g, n_band);
+  return it < n_band ? first + it : n_items;
 }
 
 template <int N>
@@ -58,7 +71,7 @@ template <int NBUF>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int kSlot = kRowsPerWave * kRowBytes;  // one wave's rows of a chunk
   __shared__ __attribute__((aligned(1024))) char ring_[4 * NBUF * kSlot];
-  const int r = item_of(a.n_q);
+  const int r = item_of(a.n_q, a.band);
   if (r >= a.n_q) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -121,7 +134,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
 template <int NBUF>
 int launch(const GatherArgs& a, hipStream_t s) {
-  const int grid = 2 * kXcds * ((a.n_q + 2 * kXcds - 1) / (2 * kXcds));
+  int grid = 2 * kXcds * slice_len_of(a.n_q);
+  if (a.band > 0 && a.band < a.n_q) {
+    const int full = a.n_q / a.band, rest = a.n_q - full * a.band;
+    grid = full * 2 * kXcds * slice_len_of(a.band) + (rest ? 2 * kXcds * slice_len_of(rest) : 0);
+  }
   hipLaunchKernelGGL(gather_kernel<NBUF>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -138,16 +155,18 @@ extern "C" {
 // workgroup). Returns 0, -1 (bad argument) or -4 (launch error). Arrays as
 // in spmla_sparse_attn (16-byte aligned device pointers; q [n_q][16][576]
 // and kv_comp [n_comp][576], kv_raw [q_pos0+n_q][576] fp16; sel
-// [n_q][top_k]; out [n_q][16][512] and lse [n_q][16] fp32).
+// [n_q][top_k]; out [n_q][16][512] and lse [n_q][16] fp32). band > 0: the
+// queries are dealt to the dies band by band, as spmla_prefill's attention
+// launch deals them.
 int spmla_ceiling_gather(const void* q, const void* kv_comp, const void* kv_raw, const int32_t* sel, float* out,
                          float* lse, int32_t n_q, int32_t q_pos0, int32_t n_comp, int32_t ratio, int32_t window,
-                         int32_t top_k, int32_t nbuf, void* stream) {
+                         int32_t top_k, int32_t nbuf, int32_t band, void* stream) {
   if (!q || !kv_raw || !sel || !out || n_q < 0 || q_pos0 < 0 || n_comp < 0 || ratio < 1 || window < 1 || top_k < 1)
     return -1;
   if (n_comp > 0 && !kv_comp) return -1;
   if (n_q == 0) return 0;
   GatherArgs a{static_cast<const char*>(q), static_cast<const char*>(kv_comp), static_cast<const char*>(kv_raw),
-               sel, out, lse, n_q, q_pos0, n_comp, ratio, window, top_k};
+               sel, out, lse, n_q, q_pos0, n_comp, ratio, window, top_k, band};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (nbuf) {
     case 2: return launch<2>(a, s);
