@@ -40,6 +40,9 @@ constexpr int kBits1 = 11;
 // at most 2,048 rows a workgroup then holds 8,256 B of static and 6,016 B of
 // dynamic LDS, so eight share a CU and a 2,048-token band runs in one round.
 constexpr int kSlack = 240;
+// Registers per thread up to which kept keys are scattered into their buckets
+// straight from registers (above it they are collected first).
+constexpr int kDirectPer = 16;
 
 // Wave-wide scans and reductions with DPP (no LDS round trips): row_shr:n
 // shifts within each 16-lane row (lanes without a source take the identity),
@@ -135,8 +138,9 @@ enum Src : int {
 };
 
 // Selection and ordering for token r of the launch. LDS: `keys` holds
-// min(top_k + kSlack, BLOCK * PER) bucketed keys, then (for the ascending
-// copy) a bitmap of the visible rows.
+// min(top_k + kSlack, BLOCK * PER) bucketed keys (and as many collected ones
+// when PER > kDirectPer), then (for the ascending copy) a bitmap of the
+// visible rows.
 template <int BLOCK, int PER, int SRC>
 __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f, int r) {
   constexpr int NW = BLOCK / 64;
@@ -388,45 +392,84 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   }
 
   // 3. Bucket the elements >= thresh (at most cap, at least nsel) for
-  // ordering: count them per bucket (the top 11 bits of key - thresh; no key
-  // exceeds key_hi), turn the counts into bucket offsets, and scatter every
-  // key from registers straight into its bucket (in any order inside it: the
-  // placement below ranks a bucket's keys by value).
+  // ordering by the top 11 bits of key - thresh (no key exceeds key_hi):
+  // counts per bucket, bucket offsets by one prefix scan, then a scatter into
+  // the buckets (in any order inside one: the placement below ranks a
+  // bucket's keys by value). With few registers per thread the kept keys are
+  // scattered straight from registers; with many (long rows, few kept) they
+  // are first collected in place order by a block-wide scan, so that the
+  // scatter loops over the few kept keys instead of every register.
   const u64 key_hi = ((u64)span << ebits) | emask;
   const u64 kspan = key_hi - thresh;
   const int kbits = kspan ? 64 - __clzll(kspan) : 0;
   const int shb = kbits > kBits1 ? kbits - kBits1 : 0;
+  u64* const bucketed = keys;
   __syncthreads();
   for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
-  __syncthreads();
+  if constexpr (PER <= kDirectPer) {
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if ((vm >> i) & 1u) {
-      const u64 key = key_of(i);
-      if (key >= thresh) atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
-    }
-  }
-  __syncthreads();
-  bucket_offsets<BLOCK>(hist, red_c);
-  u64* const bucketed = keys;
-  // Slots of up to 8 elements are claimed before any is written, so their
-  // LDS atomics are in flight together.
-  constexpr int G = PER < 8 ? PER : 8;
-#pragma unroll
-  for (int i0 = 0; i0 < PER; i0 += G) {
-    int slot[G];
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const int i = i0 + u;
-      slot[u] = -1;
+    for (int i = 0; i < PER; ++i) {
       if ((vm >> i) & 1u) {
         const u64 key = key_of(i);
-        if (key >= thresh) slot[u] = atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+        if (key >= thresh) atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
       }
     }
+    __syncthreads();
+    bucket_offsets<BLOCK>(hist, red_c);
+    // Slots of up to 8 elements are claimed before any is written, so their
+    // LDS atomics are in flight together.
+    constexpr int G = PER < 8 ? PER : 8;
 #pragma unroll
-    for (int u = 0; u < G; ++u)
-      if (slot[u] >= 0 && slot[u] < cap) bucketed[slot[u]] = key_of(i0 + u);  // < cap by construction
+    for (int i0 = 0; i0 < PER; i0 += G) {
+      int slot[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int i = i0 + u;
+        slot[u] = -1;
+        if ((vm >> i) & 1u) {
+          const u64 key = key_of(i);
+          if (key >= thresh) slot[u] = atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u)
+        if (slot[u] >= 0 && slot[u] < cap) bucketed[slot[u]] = key_of(i0 + u);  // < cap by construction
+    }
+  } else {
+    u64* const collected = keys + cap;
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) mine += (((vm >> i) & 1u) && key_of(i) >= thresh) ? 1 : 0;
+    const int mine_incl = wave_incl_scan(mine, lane);
+    if (lane == 63) red_a[wave] = mine_incl;
+    __syncthreads();
+    int pos = mine_incl - mine;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) pos += w < wave ? red_a[w] : 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if ((vm >> i) & 1u) {
+        const u64 key = key_of(i);
+        if (key >= thresh) {
+          if (pos < cap) {  // by construction
+            collected[pos] = key;
+            atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+          }
+          ++pos;
+        }
+      }
+    }
+    __syncthreads();
+    bucket_offsets<BLOCK>(hist, red_c);
+    int total_kept = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total_kept += red_a[w];
+    total_kept = min(total_kept, cap);
+    for (int e = tid; e < total_kept; e += BLOCK) {
+      const u64 key = collected[e];
+      bucketed[atomicAdd(&hist[(int)((key - thresh) >> shb)], 1)] = key;
+    }
   }
   __syncthreads();
   // After the scatter hist[b] is the end of bucket b; bucket 0 comes last, so
@@ -434,10 +477,11 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   const int n_coll = min(hist[0], cap);
   // Ascending order (optional): the winners' rows are marked in a bitmap of
   // the visible rows (nv <= kMaxComp bits), which follows the bucketed keys
-  // (the launcher reserves asc_bitmap_words(n_comp) words), and read back in
+  // and their collected copy (the launcher reserves asc_bitmap_words(n_comp)
+  // words), and read back in
   // row order after a block-wide scan of the words' popcounts.
   const int nwords = (nv + 31) >> 5;
-  unsigned* const bits = reinterpret_cast<unsigned*>(keys + cap);
+  unsigned* const bits = reinterpret_cast<unsigned*>(keys + (PER <= kDirectPer ? 1 : 2) * cap);
   if (a.sel_asc) {
     for (int i = tid; i < nwords; i += BLOCK) bits[i] = 0u;
     __syncthreads();
@@ -519,10 +563,10 @@ size_t asc_bitmap_words(int n_comp) { return ((size_t)n_comp + 31) / 32; }
 
 template <int BLOCK, int PER, int SRC>
 hipError_t launch_cfg(const TopkArgs& a, const FusedArgs& f, int grid, hipStream_t stream) {
-  // keys: the bucketed elements (at most top_k + kSlack), then the
-  // ascending-order bitmap.
+  // keys: the bucketed elements (at most top_k + kSlack), their collected
+  // copy when PER > kDirectPer, then the ascending-order bitmap.
   const int cap = std::min(a.top_k + kSlack, BLOCK * PER);
-  size_t lds = sizeof(u64) * (size_t)cap;
+  size_t lds = sizeof(u64) * (size_t)cap * (PER <= kDirectPer ? 1 : 2);
   if (a.sel_asc) lds += sizeof(unsigned) * asc_bitmap_words(a.n_comp);
   hipLaunchKernelGGL((topk_kernel<BLOCK, PER, SRC>), dim3(grid), dim3(BLOCK), lds, stream, a, f);
   return hipGetLastError();
