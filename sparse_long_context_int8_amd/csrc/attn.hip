@@ -53,7 +53,7 @@ constexpr int kRowBytes = kDqk * 2;  // 1152: one latent row
 constexpr int kXcds = 8;             // accelerator complex dies, round-robin dispatch
 
 // Work items are cut into 2 * kXcds contiguous slices of slice_len items; die
-// x takes slice 2*kXcds-1-x, then slice x (blockIdx.x = x + kXcds * l). Each
+// x takes slice 2*kXcds-1-x, then slice x (workgroup index x + kXcds * l). Each
 // die keeps runs of neighbouring queries (their window rows stay in its L2),
 // and when the cost of a query grows with its position (the first band of a
 // prefill: more visible rows) every die gets one later and one earlier slice,
