@@ -786,10 +786,11 @@ void attn_kernel(AttnArgs a) {
     // the index load for the chunk NBUF+1 places later (the order of loads
     // of the loop, where iteration ch issues chunk ch+NBUF and the indices of
     // chunk ch+2*NBUF+1).
-    load_q();
 #pragma unroll
     for (int k = 0; k <= NBUF; ++k) load_sel(c_begin + k);
-    wait_vmcnt<0>();
+    load_q();
+    static_assert(C::len(0) == C::kSteps && C::len(1) == C::kSteps, "every wave issues kSteps Q loads");
+    wait_vmcnt<C::kSteps>();  // the indices (issued before the Q loads)
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < NBUF; ++k) {
