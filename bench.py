@@ -310,15 +310,18 @@ def prepare_prefill(sp, torch, workloads, w):
 
 def time_steps(torch, w, prep, steps, warmup):
     """`warmup` untimed spmla_prefill steps, then `steps` timed ones: HIP
-    events on the launch stream around each step."""
+    events on the launch stream around each step.
+
+    The GPU leaves its sustained clocks within a few milliseconds of idling
+    and needs some 25-30 ms of work to return to them, so nothing on the host
+    stands between the work before this call, the warm-up and the timed
+    steps: the events are made first, and their times are read afterwards
+    (step_times)."""
     step = prep["step"]
-    log(f"{w.name}: warmup {warmup}")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    log(f"{w.name}: warmup {warmup}, then {steps} timed steps")
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-
-    log(f"{w.name}: timing {steps} steps")
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record()
@@ -327,9 +330,16 @@ def time_steps(torch, w, prep, steps, warmup):
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    return {"evs": evs, "wall": wall}
+
+
+def step_times(w, timed):
+    """Per-step and mean times of a time_steps run, and its throughput."""
+    evs = timed["evs"]
+    steps = len(evs) - 1
     per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     total_ms = evs[0].elapsed_time(evs[-1])
-    return {"per_step": per_step, "wall": wall, "ms_per_step": total_ms / steps,
+    return {"per_step": per_step, "wall": timed["wall"], "ms_per_step": total_ms / steps,
             "value": w.n_q * steps / (total_ms / 1e3)}
 
 
@@ -406,7 +416,7 @@ def main():
     ascending = w.n_comp * w.d_qk * 2 > ASCENDING_ROWS_ABOVE_BYTES
     n_bands = sp.spmla_num_bands(desc)
     scores_b = torch.empty((min(w.band, w.n_q), w.n_comp), dtype=torch.int32, device="cuda")
-    warm_reps, reps = 4, 20
+    warm_reps, reps = 40, 30
     # sel holds the first step's selections; the attention gets them in the
     # order spmla_prefill hands them over (prepared outside the timing).
     attn_sel = torch.cat([attn_order(torch, sel[b * w.band:min(w.n_q, (b + 1) * w.band)], ascending)
@@ -415,14 +425,29 @@ def main():
     # Attention: as the step launches it, one spmla_sparse_attn over all the
     # bands (dealt to the dies band by band). The measured ceiling: the same
     # queries through the kernel that moves the attention's bytes and computes
-    # nothing, dealt the same way, at 2, 3 and 4 chunks of loads in flight
-    # (the best counts), right after the attention launch of the same
-    # repetition, so that both see the same clocks; the first warm_reps
-    # repetitions are not counted.
+    # nothing, dealt the same way, with 2 chunks of loads in flight (its best
+    # count), right after the attention launch of the same repetition, so that
+    # both see the same clocks; the first warm_reps repetitions are not
+    # counted. 3 and 4 chunks in flight are timed in a loop of their own
+    # halfway through the uncounted repetitions (their launches,
+    # twice as long, would otherwise stand between one attention launch and
+    # the next; right before the timed steps they slow the first few dozen
+    # steps down while the GPU's power management adjusts to the steps' mix,
+    # and so would the counted repetitions), and the best of the three is the
+    # ceiling.
     ceil_lib = load_ceiling()
     sel_launches, attn_launches = [], []
     evs_c = {nbuf: [] for nbuf in (2, 3, 4)}
     for rep in range(warm_reps + reps):
+        if rep == warm_reps // 2:
+            for nbuf in (3, 4):
+                for r in range(1 + reps // 4):
+                    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    c0.record()
+                    ceiling_call(ceil_lib, torch, w, dev, attn_sel, out, lse, nbuf)
+                    c1.record()
+                    if r >= 1:
+                        evs_c[nbuf].append((c0, c1))
         for b in range(n_bands):
             a0 = b * w.band
             bn = min(w.band, w.n_q - a0)
@@ -443,14 +468,18 @@ def main():
         e1.record()
         if rep >= warm_reps:
             attn_launches.append((e0, e1))
-        for nbuf in (2, 3, 4):
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record()
-            ceiling_call(ceil_lib, torch, w, dev, attn_sel, out, lse, nbuf)
-            c1.record()
-            if rep >= warm_reps:
-                evs_c[nbuf].append((c0, c1))
-    torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        ceiling_call(ceil_lib, torch, w, dev, attn_sel, out, lse, 2)
+        c1.record()
+        if rep >= warm_reps:
+            evs_c[2].append((c0, c1))
+    # The timed steps follow right away (the breakdown's own times are read
+    # after them), then the other configurations' steps.
+    timed = time_steps(torch, w, t, args.steps, args.warmup)
+    timed_extra = {name: time_steps(torch, workloads.BY_NAME[name], te, args.steps, args.warmup)
+                   for name, te in extras.items()}
+
     t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in sel_launches]))
     t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in sel_launches]))
     t_attn = float(np.mean([e0.elapsed_time(e1) for e0, e1 in attn_launches]))
@@ -458,7 +487,7 @@ def main():
     best_nbuf = min(t_ceil_by_nbuf, key=t_ceil_by_nbuf.get)
     t_ceil = t_ceil_by_nbuf[best_nbuf]
 
-    t.update(time_steps(torch, w, t, args.steps, args.warmup))
+    t.update(step_times(w, timed))
     per_step, wall, ms_per_step, value = t["per_step"], t["wall"], t["ms_per_step"], t["value"]
 
     bytes_q = attn_bytes_per_query(w)
@@ -546,7 +575,7 @@ def main():
         # the same steps and warm-up, right after the headline's.
         for name, te in extras.items():
             we = workloads.BY_NAME[name]
-            te.update(time_steps(torch, we, te, args.steps, args.warmup))
+            te.update(step_times(we, timed_extra[name]))
             res["workloads"][name] = {
                 "n_q": we.n_q, "q_pos0": we.q_pos0, "top_k": we.top_k, "bands": sp.spmla_num_bands(te["desc"]),
                 "ms_per_step": round(te["ms_per_step"], 4),
