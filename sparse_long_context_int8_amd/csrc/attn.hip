@@ -143,6 +143,25 @@ __device__ __forceinline__ unsigned long long lds_read_u64(unsigned addr) {
   asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
+// The same reads at base + OFF with OFF in the instruction's 16-bit offset
+// field when it fits (a chunk buffer's offset and a read's fixed part then
+// cost no address arithmetic per read).
+template <int OFF>
+__device__ __forceinline__ half8 lds_read_b128_at(unsigned base) {
+  static_assert(OFF >= 0, "offset");
+  half8 v;
+  if constexpr (OFF <= 65535) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF));
+  else asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(base + OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ short4v lds_read_tr16_at(unsigned base) {
+  static_assert(OFF >= 0, "offset");
+  short4v v;
+  if constexpr (OFF <= 65535) asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF));
+  else asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(base + OFF));
+  return v;
+}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Waits until at most N LDS operations are outstanding (they complete in
 // issue order); N fits the 4-bit counter.
@@ -223,6 +242,15 @@ __device__ __forceinline__ void with_slice(int h, F&& f) {
     if (h == N - 1) f(std::integral_constant<int, N - 1>{});
     else with_slice<N - 1>(h, f);
   }
+}
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Max and sum over the four lanes l, l^16, l^32, l^48 (one head's keys)
@@ -487,22 +515,51 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // One chunk in `cur`. After the S^T exchange barrier `cur` is no longer
-  // read, and stage(0) .. stage(4) may refill it: stage 0 is called right
+  // Per-lane LDS addresses of this wave's K and V^T fragment reads in buffer
+  // 0 (the buffer's offset and the fixed part of each read go in the read's
+  // offset field). K: key row n = 16*tile + c16, k-step ks < 16 at
+  // k_base[ks & 3] + 256*(ks >> 2) (the row swizzle only permutes the low four
+  // 16-byte units, i.e. ks & 3 and g), k-steps 16 and 17 (rope dims) at
+  // r_base[ks - 16]. V^T: output tile nt, unit u of PV step kb at
+  // v_base[nt][u] + 1024*kPvKeys*kb (the swizzle depends only on the low
+  // four row bits, which kPvKeys*kb leaves alone).
+  const unsigned bufs_addr = (unsigned)(uintptr_t)bufs;
+  unsigned k_base[4], r_base[2], v_base[C::kNt][kUnits];
+  {
+    const int n = 16 * tile + c16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k_base[j] = bufs_addr + n * 1024 + (((4 * j + g) ^ swz_a(n)) << 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r_base[j] = bufs_addr + C::kBufA + n * 128 + (((4 * j + g) ^ swz_b(n)) << 4);
+    const int tri = (lane >> 2) & 3;
+    const int trc = lane & 3;
+#pragma unroll
+    for (int nt = 0; nt < C::kNt; ++nt) {
+      const int dv0 = (kDv / WAVES) * wave + 16 * nt;
+      const int unit = (dv0 >> 3) + (trc >> 1);
+      const int sub = (trc & 1) << 3;
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u) {
+        const int nr = kKpl * g + 4 * u + tri;
+        v_base[nt][u] = bufs_addr + nr * 1024 + ((unit ^ swz_a(nr)) << 4) + sub;
+      }
+    }
+  }
+
+  // One chunk in buffer buf_c. After the S^T exchange barrier the buffer is
+  // no longer read, and stage(0) .. stage(4) may refill it: stage 0 is called right
   // after the S^T reads are issued (before their wait), stages 1-4 between
   // the steps of the softmax, so that the loads of the next gather reach the
   // memory pipeline spread out rather than in one burst. No barrier is
   // needed at the end of a chunk: the S^T area is written again only after a
   // later chunk's barrier, which every wave reaches after its last read of it.
-  auto compute = [&](lds_char* cur, unsigned long long valid_in, unsigned valid_lds, int sb, auto&& stage) {
-    const unsigned bA = (unsigned)(uintptr_t)cur;  // LDS byte address
+  auto compute = [&](auto buf_c, unsigned long long valid_in, unsigned valid_lds, int sb, auto&& stage) {
+    constexpr int BOFF = decltype(buf_c)::value * C::kBuf;  // the chunk buffer's offset from bufs
     float* sbuf_c = sbuf_g + sb * (C::kSBytes / 4);
     const unsigned sbuf_c_addr = sbuf_addr + sb * C::kSBytes;
 
     // V^T fragments: O^T[dims (512/W) wave + 16nt + 4g + i][head c16] needs,
     // per PV step, keys kPvKeys*kb + kKpl*g + 4u + tri of dims dv0 + 4*trc ..
-    const int tri = (lane >> 2) & 3;
-    const int trc = lane & 3;
     // Streaming reads them before the S^T exchange (its buffer is refilled
     // right after it), in two halves issued behind the K fragments so that
     // the first QK products need not wait for them; the pair variant, which
@@ -516,16 +573,12 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int nt = 0; nt < C::kNt; ++nt) {
         if (nt < nt_begin || nt >= nt_end) continue;
-        const int dv0 = (kDv / WAVES) * wave + 16 * nt;
-        const int unit = (dv0 >> 3) + (trc >> 1);
-        const int sub = (trc & 1) << 3;
+        static_for<C::kPvSteps>([&](auto kb_c) {
+          constexpr int KB = decltype(kb_c)::value;
 #pragma unroll
-        for (int kb = 0; kb < C::kPvSteps; ++kb)
-#pragma unroll
-          for (int u = 0; u < kUnits; ++u) {
-            const int n = C::kPvKeys * kb + kKpl * g + 4 * u + tri;
-            vt[nt][kb][u] = lds_read_tr16(bA + n * 1024 + ((unit ^ swz_a(n)) << 4) + sub);
-          }
+          for (int u = 0; u < kUnits; ++u)
+            vt[nt][KB][u] = lds_read_tr16_at<BOFF + C::kPvKeys * KB * 1024>(v_base[nt][u]);
+        });
       }
     };
     auto fence_v = [&]() {
@@ -542,7 +595,6 @@ void attn_kernel(AttnArgs a) {
     // K read address is fixed at compile time (no per-read branches).
     auto qk = [&](auto half_c) {
       constexpr int HALF = decltype(half_c)::value;
-      const int n = 16 * tile + c16;
       constexpr int kLen = C::len(HALF);
       constexpr int kStart = C::start(HALF);
       // K fragments in two batches (fewer live registers). Streaming issues
@@ -551,24 +603,22 @@ void attn_kernel(AttnArgs a) {
       // follow the products, and the exchange barrier's wait covers them.
       constexpr int kBatch = (kLen + 1) / 2;
       static_assert(kLen > kBatch, "two K batches");
-      auto read_k = [&](half8(&kf)[kBatch], int s0, int cnt) {
-#pragma unroll
-        for (int s = 0; s < kBatch; ++s) {
-          const int ks = kStart + s0 + s;  // k-step of 32 latent dims
-          if (s < cnt) {
-            if (ks < 16) {
-              kf[s] = lds_read_b128(bA + n * 1024 + (((4 * ks + g) ^ swz_a(n)) << 4));
-            } else {
-              kf[s] = lds_read_b128(bA + C::kBufA + n * 128 + (((4 * (ks - 16) + g) ^ swz_b(n)) << 4));
-            }
+      auto read_k = [&](half8(&kf)[kBatch], auto s0_c, auto cnt_c) {
+        static_for<decltype(cnt_c)::value>([&](auto s_c) {
+          constexpr int S = decltype(s_c)::value;
+          constexpr int KS = kStart + decltype(s0_c)::value + S;  // k-step of 32 latent dims
+          if constexpr (KS < 16) {
+            kf[S] = lds_read_b128_at<BOFF + 256 * (KS >> 2)>(k_base[KS & 3]);
+          } else {
+            kf[S] = lds_read_b128_at<BOFF>(r_base[KS - 16]);
           }
-        }
+        });
       };
       // Three independent accumulation chains, summed in a fixed order.
       float4v sacc[3] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
       {
         half8 kf[kBatch];
-        read_k(kf, 0, kBatch);
+        read_k(kf, std::integral_constant<int, 0>{}, std::integral_constant<int, kBatch>{});
         lds_wait();
 #pragma unroll
         for (int s = 0; s < kBatch; ++s) fence_reg(kf[s]);
@@ -578,7 +628,7 @@ void attn_kernel(AttnArgs a) {
       }
       {
         half8 kf[kBatch];
-        read_k(kf, kBatch, kLen - kBatch);
+        read_k(kf, std::integral_constant<int, kBatch>{}, std::integral_constant<int, kLen - kBatch>{});
         if constexpr (kEarlyV) {
           read_v(0, kNtHalf);
           lds_wait_n<kVReadsHalf>();
@@ -737,7 +787,10 @@ void attn_kernel(AttnArgs a) {
   };
 
   if constexpr (GROUP == 1) {
-    auto buf_of = [&](int ch) { return bufs + ((unsigned)ch % NBUF) * C::kBuf; };
+    // Chunk ch of this work item lives in ring buffer (ch - c_begin) mod NBUF:
+    // the loop below, unrolled by NBUF, then computes from a buffer known at
+    // compile time.
+    auto buf_of = [&](int ch) { return bufs + ((unsigned)(ch - c_begin) % NBUF) * C::kBuf; };
     // Gather of chunk ch into its ring buffer and its validity mask into its
     // slot; its selected indices are already in LDS. Split into the stages
     // of compute(): 0 reads the indices, 1 forms the row pointers, the mask
@@ -796,16 +849,20 @@ void attn_kernel(AttnArgs a) {
     for (int k = 0; k < NBUF; ++k) {
       if (c_begin + k < c_end) issue(c_begin + k);  // includes the index load NBUF + 1 chunks ahead
     }
-    for (int ch = c_begin; ch < c_end; ++ch) {
-      // Chunk ch's loads (and all before them) are complete once at most
-      // kWaitAhead later ones are outstanding, provided the chunks up to
-      // ch+NBUF-1 were all issued; near the end, wait for everything.
-      if (ch + NBUF - 1 < c_end) wait_vmcnt<C::kWaitAhead>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      const bool refill = ch + NBUF < c_end;  // uniform
-      compute(buf_of(ch), 0ull, valid_addr + 8u * ((unsigned)ch % C::kSlots), 0, [&](auto st_c) {
-        if (refill) issue_stage(ch + NBUF, st_c);
+    for (int ch0 = c_begin; ch0 < c_end; ch0 += NBUF) {
+      static_for<NBUF>([&](auto b_c) {
+        const int ch = ch0 + decltype(b_c)::value;
+        if (ch >= c_end) return;  // uniform
+        // Chunk ch's loads (and all before them) are complete once at most
+        // kWaitAhead later ones are outstanding, provided the chunks up to
+        // ch+NBUF-1 were all issued; near the end, wait for everything.
+        if (ch + NBUF - 1 < c_end) wait_vmcnt<C::kWaitAhead>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        const bool refill = ch + NBUF < c_end;  // uniform
+        compute(b_c, 0ull, valid_addr + 8u * ((unsigned)ch % C::kSlots), 0, [&](auto st_c) {
+          if (refill) issue_stage(ch + NBUF, st_c);
+        });
       });
     }
     wait_vmcnt<0>();  // index loads for chunks past the end
@@ -827,18 +884,18 @@ void attn_kernel(AttnArgs a) {
     };
     unsigned long long valid_cur = gather_pair(c_begin, buf0);
     load_q();
-    auto step = [&](int ch, lds_char* cur, lds_char* nxt) {
+    auto step = [&](int ch, auto cur_c, lds_char* nxt) {
       wait_vmcnt<0>();
       lds_barrier();
       unsigned long long valid_next = 0;
       if (ch + 1 < c_end) valid_next = gather_pair(ch + 1, nxt);
-      compute(cur, valid_cur, 0u, ch & 1, [](auto) {});
+      compute(cur_c, valid_cur, 0u, ch & 1, [](auto) {});
       valid_cur = valid_next;
     };
     for (int ch = c_begin;;) {
-      step(ch, buf0, buf1);
+      step(ch, std::integral_constant<int, 0>{}, buf1);
       if (++ch >= c_end) break;
-      step(ch, buf1, buf0);
+      step(ch, std::integral_constant<int, 1>{}, buf0);
       if (++ch >= c_end) break;
     }
   }
