@@ -88,8 +88,6 @@ size_t scores_bytes_per_band(const spmla_desc* d) {
 }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr size_t kRowBytes = (size_t)spmla::kDqk * 2;  // one fp16 latent row
-constexpr size_t kDieL2Bytes = (size_t)4 << 20;        // L2 of one accelerator die
 
 // Selection groups: consecutive bands that select the same way get one set
 // of selection launches for all their queries, while the group's scratch
@@ -207,7 +205,7 @@ int run_prefill(const spmla_desc* d, const uint16_t* q, const uint16_t* kv_comp,
   // compressed rows outgrow one die's L2: the queries in flight on a die then
   // sweep the rows together and share what they gather (the softmax does not
   // depend on the order of its keys).
-  const bool ascending = (size_t)d->n_comp * kRowBytes > kDieL2Bytes;
+  const bool ascending = spmla::rows_beyond_l2(d->n_comp);
 
   for_each_group(d, gb, [&](int64_t g0, int64_t g1, bool fused) {
     if (rc) return;

@@ -293,7 +293,16 @@ constexpr float kRescaleThreshold = 8.0f;
 // ws0 .. t1). Wave group g (waves g*WAVES ..) runs the streaming per-chunk
 // work for query t_g with its own mask; every gathered row is read once for
 // both queries.
-template <int WAVES, int CHUNK, int NBUF, int WPE, int GROUP>
+// FAR: the gathered rows come from beyond the dies' L2 (compressed rows
+// larger than one die's L2; the selection then arrives in ascending row
+// order). The loads of a chunk's gather are then spread over the whole
+// softmax, and a chunk's head maxima are formed before the test for a new
+// reference (their exchange across lanes also spaces two gather stages).
+// Otherwise (L2-resident rows) the head maxima are formed only when some
+// lane's own maximum calls for a new reference, and the last two gather
+// stages follow the exponentials and half of the PV products: the shorter
+// per-chunk chain matters more there than the spacing of the loads.
+template <int WAVES, int CHUNK, int NBUF, int WPE, int GROUP, bool FAR>
 __global__ __launch_bounds__(64 * WAVES * GROUP) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_kernel(AttnArgs a) {
   using C = Cfg<WAVES, CHUNK, NBUF, WPE, GROUP>;
@@ -549,8 +558,9 @@ void attn_kernel(AttnArgs a) {
   // One chunk in buffer buf_c. After the S^T exchange barrier the buffer is
   // no longer read, and stage(0) .. stage(4) may refill it: stage 0 is called right
   // after the S^T reads are issued (before their wait), stages 1-4 between
-  // the steps of the softmax, so that the loads of the next gather reach the
-  // memory pipeline spread out rather than in one burst. No barrier is
+  // the steps of the softmax (FAR) or of the softmax and the PV products, so
+  // that the loads of the next gather reach the memory pipeline spread out
+  // rather than in one burst. No barrier is
   // needed at the end of a chunk: the S^T area is written again only after a
   // later chunk's barrier, which every wave reaches after its last read of it.
   auto compute = [&](auto buf_c, unsigned long long valid_in, unsigned valid_lds, int sb, auto&& stage) {
@@ -716,21 +726,31 @@ void attn_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     stage(std::integral_constant<int, 2>{});
     __builtin_amdgcn_sched_barrier(0);
-    cmax = max4_heads(cmax) * a.scale_log2e;  // scale > 0, so the max commutes with it
     // Move the reference (and rescale O and l) only when needed; the test is
-    // made per head and the branch is taken if any head needs it.
-    const bool move = cmax > m_ref + kRescaleThreshold;
-    if (__ballot(move)) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - cmax) : 1.f;
-      if (move) m_ref = cmax;
+    // made per head on the head's maximum hmax (scale > 0, so the maximum
+    // commutes with it). A lane holds a quarter of its head's keys, and no
+    // head needs a new reference unless some lane's own maximum does.
+    auto move_ref = [&](float hmax) {
+      const bool move = hmax > m_ref + kRescaleThreshold;
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - hmax) : 1.f;
+      if (move) m_ref = hmax;
       l_run *= alpha;
 #pragma unroll
       for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] *= alpha;
+    };
+    if constexpr (FAR) {
+      const float hmax = max4_heads(cmax) * a.scale_log2e;
+      if (__ballot(hmax > m_ref + kRescaleThreshold)) move_ref(hmax);
+    } else {
+      const float lmax = cmax * a.scale_log2e;
+      if (__ballot(lmax > m_ref + kRescaleThreshold)) move_ref(max4_heads(lmax));
     }
     float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
     fence_reg(m_use);
-    __builtin_amdgcn_sched_barrier(0);
-    stage(std::integral_constant<int, 3>{});
+    if constexpr (FAR) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(std::integral_constant<int, 3>{});
+    }
     __builtin_amdgcn_sched_barrier(0);
     using pvec = std::conditional_t<kKpl == 8, half8, half4>;
     pvec pf[C::kPvSteps];
@@ -748,7 +768,7 @@ void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < C::kPvSteps; ++kb) fence_reg(pf[kb]);
     fence_reg(l_run);
     __builtin_amdgcn_sched_barrier(0);
-    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, FAR ? 4 : 3>{});
     __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T . P^T
@@ -756,6 +776,11 @@ void attn_kernel(AttnArgs a) {
     for (int nt = 0; nt < C::kNt; ++nt)
 #pragma unroll
       for (int kb = 0; kb < C::kPvSteps; ++kb) {
+        if (!FAR && nt == C::kNt / 2 && kb == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          stage(std::integral_constant<int, 4>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (kKpl == 8) {
           const half4 hlo = __builtin_bit_cast(half4, vt[nt][kb][0]);
           const half4 hhi = __builtin_bit_cast(half4, vt[nt][kb][1]);
@@ -1048,8 +1073,12 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t stream) {
     grid = full * 2 * kXcds * attn_slice_len(a.band_items) + (rest ? 2 * kXcds * attn_slice_len(rest) : 0);
   }
   constexpr int W = SPMLA_ATTN_WAVES;
-  hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE, 1>),
-                     dim3(grid), dim3(64 * W), 0, stream, a);
+  if (rows_beyond_l2(a.n_comp))
+    hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE, 1, true>),
+                       dim3(grid), dim3(64 * W), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<W, SPMLA_ATTN_CHUNK, SPMLA_ATTN_NBUF, SPMLA_ATTN_WPE, 1, false>),
+                       dim3(grid), dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(a.n_q * kHeads * kMergeParts), dim3(kMergeCols * kMergeGroups), 0,
@@ -1067,7 +1096,7 @@ hipError_t launch_attn_grouped(const AttnArgs& a_in, hipStream_t stream) {
   // Bitmaps of the two queries' rows and the pair's row list.
   const size_t words = ((size_t)a.n_comp + 31) / 32;
   const size_t lds = 4 * (2 * words + 2 * (size_t)a.top_k);
-  hipLaunchKernelGGL((attn_kernel<SPMLA_ATTN_WAVES, SPMLA_ATTN_CHUNK, 2, SPMLA_ATTN_WPE, 2>),
+  hipLaunchKernelGGL((attn_kernel<SPMLA_ATTN_WAVES, SPMLA_ATTN_CHUNK, 2, SPMLA_ATTN_WPE, 2, false>),
                      dim3(grid), dim3(128 * SPMLA_ATTN_WAVES), lds, stream, a);
   return hipGetLastError();
 }
