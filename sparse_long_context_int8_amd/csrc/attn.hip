@@ -296,8 +296,9 @@ constexpr float kRescaleThreshold = 8.0f;
 // FAR: the gathered rows come from beyond the dies' L2 (compressed rows
 // larger than one die's L2; the selection then arrives in ascending row
 // order). The loads of a chunk's gather are then spread over the whole
-// softmax, and a chunk's head maxima are formed before the test for a new
-// reference (their exchange across lanes also spaces two gather stages).
+// softmax, a chunk's head maxima are formed before the test for a new
+// reference (their exchange across lanes also spaces two gather stages), and
+// the softmax sums come from the matrix cores.
 // Otherwise (L2-resident rows) the head maxima are formed only when some
 // lane's own maximum calls for a new reference, and the last two gather
 // stages follow the exponentials and half of the PV products: the shorter
@@ -441,6 +442,10 @@ void attn_kernel(AttnArgs a) {
   for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] = float4v{0.f, 0.f, 0.f, 0.f};
   float m_ref = -__builtin_inff();  // softmax reference (log2 domain) of head c16
   float l_run = 0.f;                // this lane's share of the softmax sum
+  // FAR: the softmax sum of head c16 (all four entries) instead, as the PV
+  // product of a tile of ones with the same fp16 probabilities (one more
+  // product per chunk in place of the adds, which measured faster there).
+  float4v acc_l = float4v{0.f, 0.f, 0.f, 0.f};
 
   // Streaming: the selected indices of chunk ch land in sel_ring slot
   // ch mod kSlots (lanes < CHUNK, each a 4-byte global->LDS load; every wave
@@ -454,17 +459,19 @@ void attn_kernel(AttnArgs a) {
   };
   // Streaming: row of key `key` of the query's list given its selected index
   // (used when key < nsel), and whether the query uses it.
+  // Branch-free (selects only); a key the query does not use points at the
+  // query's own raw row, a valid address whose contribution is masked. Row
+  // offsets fit 32 bits: rows < 4 * kMaxComp + 4 (host-checked), and
+  // 131,076 * 1,152 < 2^32.
+  static_assert((4ull * kMaxComp + 4) * kRowBytes < (1ull << 32), "32-bit row offsets");
   auto row_ptr = [&](int key, int selv, bool& ok) -> const char* {
-    const char* p = self_row;
-    ok = false;
-    if (key < nsel) {
-      ok = (selv >= 0) && (selv < nv);
-      if (ok) p = comp_base + (int64_t)selv * kRowBytes;
-    } else if (key < nk) {
-      ok = true;
-      p = raw_base + (int64_t)(ws + key - nsel) * kRowBytes;
-    }
-    return p;
+    const bool is_sel = key < nsel;
+    const bool sel_ok = (unsigned)selv < (unsigned)nv;
+    ok = is_sel ? sel_ok : key < nk;
+    const bool comp = is_sel && sel_ok;
+    const int raw = (is_sel || key >= nk) ? t : ws + key - nsel;
+    const unsigned off = (unsigned)(comp ? selv : raw) * (unsigned)kRowBytes;
+    return (comp ? comp_base : raw_base) + off;
   };
   // Pair variant: row pointer of key ch*CHUNK + lane of the pair's list, and
   // whether this group's query uses it.
@@ -734,7 +741,8 @@ void attn_kernel(AttnArgs a) {
       const bool move = hmax > m_ref + kRescaleThreshold;
       const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - hmax) : 1.f;
       if (move) m_ref = hmax;
-      l_run *= alpha;
+      if constexpr (FAR) acc_l *= alpha;
+      else l_run *= alpha;
 #pragma unroll
       for (int nt = 0; nt < C::kNt; ++nt) acc_o[nt] *= alpha;
     };
@@ -760,10 +768,10 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < kKpl; ++i) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zz[kb][i], a.scale_log2e, -m_use));
-        psum += p;
+        if constexpr (!FAR) psum += p;
         pf[kb][i] = (_Float16)p;
       }
-    l_run += psum;
+    if constexpr (!FAR) l_run += psum;
 #pragma unroll
     for (int kb = 0; kb < C::kPvSteps; ++kb) fence_reg(pf[kb]);
     fence_reg(l_run);
@@ -791,6 +799,18 @@ void attn_kernel(AttnArgs a) {
           acc_o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf[kb], acc_o[nt], 0, 0, 0);
         }
       }
+    if constexpr (FAR) {
+#pragma unroll
+      for (int kb = 0; kb < C::kPvSteps; ++kb) {
+        if constexpr (kKpl == 8) {
+          const half8 ones = half8{1, 1, 1, 1, 1, 1, 1, 1};
+          acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[kb], acc_l, 0, 0, 0);
+        } else {
+          const half4 ones = half4{1, 1, 1, 1};
+          acc_l = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pf[kb], acc_l, 0, 0, 0);
+        }
+      }
+    }
   };
 
   if (c_begin >= c_end) {  // an empty split: a neutral partial
@@ -927,7 +947,7 @@ void attn_kernel(AttnArgs a) {
     }
   }
 
-  const float l_tot = sum4_heads(l_run);
+  const float l_tot = FAR ? acc_l[0] : sum4_heads(l_run);
   if (a.splits > 1) {
     // Partial result of this split: O and l relative to the reference m
     // (log2 units); attn_merge_kernel combines the splits of a query.
