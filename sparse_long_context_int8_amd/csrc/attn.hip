@@ -464,14 +464,20 @@ void attn_kernel(AttnArgs a) {
   // offsets fit 32 bits: rows < 4 * kMaxComp + 4 (host-checked), and
   // 131,076 * 1,152 < 2^32.
   static_assert((4ull * kMaxComp + 4) * kRowBytes < (1ull << 32), "32-bit row offsets");
+  // The two bases held in vector registers (the selects below take them
+  // from there instead of copying them from scalar registers per call).
+  const char* comp_base_v = comp_base;
+  const char* raw_base_v = raw_base;
+  fence_reg(comp_base_v);
+  fence_reg(raw_base_v);
   auto row_ptr = [&](int key, int selv, bool& ok) -> const char* {
     const bool is_sel = key < nsel;
     const bool sel_ok = (unsigned)selv < (unsigned)nv;
     ok = is_sel ? sel_ok : key < nk;
     const bool comp = is_sel && sel_ok;
     const int raw = (is_sel || key >= nk) ? t : ws + key - nsel;
-    const unsigned off = (unsigned)(comp ? selv : raw) * (unsigned)kRowBytes;
-    return (comp ? comp_base : raw_base) + off;
+    const unsigned off = __umul24((unsigned)(comp ? selv : raw), (unsigned)kRowBytes);
+    return (comp ? comp_base_v : raw_base_v) + off;
   };
   // Pair variant: row pointer of key ch*CHUNK + lane of the pair's list, and
   // whether this group's query uses it.
