@@ -674,7 +674,12 @@ void attn_kernel(AttnArgs a) {
       const int slot = s_slot<CHUNK>(4 * tile + g, c16);
       *reinterpret_cast<float4v*>(&sbuf_c[(HALF * kHeads + c16) * C::kSStride + 4 * slot]) = ssum;
     };
+    // L2-resident rows: the wave's QK products and their K reads go first on
+    // its SIMD (a raised wave priority), which measured 0.3% faster per
+    // prefill step; for rows beyond the L2 it measured slower.
+    if constexpr (!FAR) __builtin_amdgcn_s_setprio(1);
     with_slice<C::kHalves>(half, qk);
+    if constexpr (!FAR) __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // also completes this wave's V^T and mask reads
     if constexpr (kEarlyV) {
       fence_v();
