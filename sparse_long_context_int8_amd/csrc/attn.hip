@@ -461,8 +461,8 @@ void attn_kernel(AttnArgs a) {
   // (used when key < nsel), and whether the query uses it.
   // Branch-free (selects only); a key the query does not use points at the
   // query's own raw row, a valid address whose contribution is masked. Row
-  // offsets fit 32 bits: rows < 4 * kMaxComp + 4 (host-checked), and
-  // 131,076 * 1,152 < 2^32.
+  // offsets fit 32 bits and both factors 24 (the full-rate 24-bit multiply):
+  // rows < 4 * kMaxComp + 4 (host-checked), and 131,076 * 1,152 < 2^32.
   static_assert((4ull * kMaxComp + 4) * kRowBytes < (1ull << 32), "32-bit row offsets");
   // The two bases held in vector registers (the selects below take them
   // from there instead of copying them from scalar registers per call).
