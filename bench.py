@@ -258,23 +258,26 @@ def bench_attn_grouped(args, sp, workloads, torch):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     n_bands = sp.spmla_num_bands(desc)
-    res = {}
-    for name, fn in (("streaming", sp.spmla_sparse_attn), ("grouped", sp.spmla_sparse_attn_grouped)):
-        times = []
-        for rep in range(args.warmup + args.steps):
-            for b in range(n_bands):
-                a0 = b * w.band
-                bn = min(w.band, w.n_q - a0)
-                d = sp.make_desc(bn, w.q_pos0 + a0, w.window, w.top_k, ratio=w.ratio, band=w.band, n_raw=w.n_raw)
+    # The two kernels alternate band by band in every pass, so that both see
+    # the same clocks; the first `warmup` passes are not counted.
+    kernels = (("streaming", sp.spmla_sparse_attn), ("grouped", sp.spmla_sparse_attn_grouped))
+    times = {name: [] for name, _ in kernels}
+    band_sel = [sel[b * w.band:min(w.n_q, (b + 1) * w.band)].contiguous() for b in range(n_bands)]
+    for rep in range(args.warmup + args.steps):
+        for b in range(n_bands):
+            a0 = b * w.band
+            bn = min(w.band, w.n_q - a0)
+            d = sp.make_desc(bn, w.q_pos0 + a0, w.window, w.top_k, ratio=w.ratio, band=w.band, n_raw=w.n_raw)
+            for name, fn in kernels:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                fn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"], sel[a0:a0 + bn].contiguous(),
-                   out[a0:a0 + bn], lse[a0:a0 + bn])
+                fn(d, dev["q"][a0:a0 + bn], dev["kv_comp"], dev["kv_raw"], band_sel[b], out[a0:a0 + bn],
+                   lse[a0:a0 + bn])
                 e1.record(stream)
                 if rep >= args.warmup:
-                    times.append((e0, e1))
-        torch.cuda.synchronize()
-        res[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in times]))
+                    times[name].append((e0, e1))
+    torch.cuda.synchronize()
+    res = {name: float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) for name, ev in times.items()}
     bytes_q = attn_bytes_per_query(w)
     per_launch = float(bytes_q.sum()) / n_bands
     print(json.dumps({
