@@ -741,6 +741,58 @@ def test_topk_extreme_scores(sp):
     np.testing.assert_array_equal(sel.cpu().numpy(), want)
 
 
+def _long_row_scores(rng, n_q, n_comp):
+    """Score rows over ~30,500 rows, one pattern per row: clustered and
+    spread values, the whole int32 range, negatives only, winners only off
+    or only on a regular grid of positions (one 64-row run in eight per
+    1,024 rows), ties around the k-th score, one value, and values next to
+    powers of two."""
+    e = np.arange(n_comp)
+    strided = ((e >> 10) % 8) == (((e & 1023) >> 6) % 8)
+    rows = []
+    rows.append(np.rint(rng.standard_normal(n_comp) * 1000.0))
+    rows.append(rng.integers(-(2**31) + 1, 2**31 - 1, n_comp, dtype=np.int64))
+    rows.append(rng.integers(-(2**31) + 1, -1, n_comp, dtype=np.int64))
+    r = rng.integers(0, 1000, n_comp)
+    r[~strided & (rng.random(n_comp) < 0.5)] += 5000
+    rows.append(r)
+    r = rng.integers(0, 1000, n_comp)
+    r[strided] += 5000
+    rows.append(r)
+    r = rng.integers(0, 9, n_comp)
+    r[rng.permutation(n_comp)[:1500]] = 10
+    rows.append(r)
+    rows.append(np.full(n_comp, 77))
+    p2 = 1 << rng.integers(5, 30, n_comp)
+    rows.append(p2 + rng.integers(-1, 2, n_comp))
+    sc = np.stack([rows[i % len(rows)] for i in range(n_q)]).astype(np.int32)
+    return sc
+
+
+@pytest.mark.parametrize("k", [1, 2048, 4096])
+def test_topk_long_rows(sp, k):
+    """Dense selection over rows of ~30,500 visible compressed rows (the
+    decode and verification shape, 32 scores per thread) for the score
+    patterns above: indices and counts bit-exact."""
+    import torch
+
+    rng = np.random.default_rng(70 + k)
+    n_q, q_pos0 = 8, 122000
+    n_comp = (q_pos0 + n_q) // 4
+    say(f"[parity long-row top-k] k={k} n_comp={n_comp}")
+    sc = _long_row_scores(rng, n_q, n_comp)
+    for r in range(n_q):
+        sc[r, oracle.n_visible(q_pos0 + r, n_comp, 4):] = oracle.INVISIBLE
+    d = sp.make_desc(n_q, q_pos0, 16, k)
+    sel = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((n_q,), dtype=torch.int32, device="cuda")
+    sp.spmla_topk(d, torch.from_numpy(sc).cuda(), sel, n_sel)
+    torch.cuda.synchronize()
+    want, want_n = oracle.topk_select(sc, q_pos0, 4, k, n_comp)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want)
+    np.testing.assert_array_equal(n_sel.cpu().numpy(), want_n)
+
+
 def test_lse_natural_log(sp):
     """q = 0 makes every logit 0, so lse = log(number of keys) exactly-ish."""
     import torch
