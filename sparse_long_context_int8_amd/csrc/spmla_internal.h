@@ -19,7 +19,7 @@ constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxComp = 32768;
-constexpr int kMaxSplits = 64;  // key splits per query of a small call
+constexpr int kMaxSplits = 32;  // key splits per query of a small call
 constexpr size_t kDieL2Bytes = (size_t)4 << 20;  // L2 of one accelerator die
 // Compressed rows beyond one die's L2: the attention then gathers them from
 // MALL or HBM, in ascending row order (spmla_prefill hands it the selection

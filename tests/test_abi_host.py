@@ -133,12 +133,12 @@ def test_workspace_bytes():
 
 def test_workspace_covers_split_partials_and_fused_candidates():
     """Small calls need room for the attention's key-split partials (up to
-    64 splits x [16][512] + (m, l) per query); long-history bands need the
+    32 splits x [16][512] + (m, l) per query); long-history bands need the
     fused selection's slots; both fit the scratch the call reports."""
     per_split = (16 * 512 + 16 * 2) * 4
     for w in (workloads.DECODE_1, workloads.VERIFY_5):
         nb = sp.spmla_prefill_workspace_bytes(desc_of(w))
-        splits = min(64, -(-1024 // w.n_q))
+        splits = min(32, -(-1024 // w.n_q))
         assert nb >= w.n_q * splits * per_split
     d = sp.make_desc(300, 6000, 128, 512)  # 300 queries: 4 splits each
     assert sp.spmla_prefill_workspace_bytes(d) >= 300 * 4 * per_split
