@@ -438,9 +438,21 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     }
   } else {
     u64* const collected = keys + cap;
+    // key_of(i) >= thresh from 32-bit parts, without forming the key (most
+    // elements of a long row fail it): a score above ts, or equal to it at a
+    // row of at most jm (thresh >> ebits <= span, so ts <= vmax). Dense and
+    // recomputed elements past the visible rows hold INT32_MIN at a row >= nv
+    // > jm and so never pass; candidate slots past their count carry no row
+    // and are masked by vm. ts and jm are block-uniform (scalar registers).
+    const int ts = __builtin_amdgcn_readfirstlane((int)((unsigned)vmin + (unsigned)(thresh >> ebits)));
+    const int jm = __builtin_amdgcn_readfirstlane(nv - 1 - (int)(thresh & emask));
+    auto kept_of = [&](int i) -> bool {
+      const bool pass = sc[i] > ts || (sc[i] == ts && (SRC == kCandidate ? jx[i] <= jm : tid <= jm - i * BLOCK));
+      return SRC == kCandidate ? (((vm >> i) & 1u) && pass) : pass;
+    };
     int mine = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) mine += (((vm >> i) & 1u) && key_of(i) >= thresh) ? 1 : 0;
+    for (int i = 0; i < PER; ++i) mine += kept_of(i) ? 1 : 0;
     const int mine_incl = wave_incl_scan(mine, lane);
     if (lane == 63) red_a[wave] = mine_incl;
     __syncthreads();
@@ -449,15 +461,13 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     for (int w = 0; w < NW; ++w) pos += w < wave ? red_a[w] : 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if ((vm >> i) & 1u) {
-        const u64 key = key_of(i);
-        if (key >= thresh) {
-          if (pos < cap) {  // by construction
-            collected[pos] = key;
-            atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
-          }
-          ++pos;
+      if (kept_of(i)) {
+        if (pos < cap) {  // by construction
+          const u64 key = key_of(i);
+          collected[pos] = key;
+          atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
         }
+        ++pos;
       }
     }
     __syncthreads();
