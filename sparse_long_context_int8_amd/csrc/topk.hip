@@ -178,12 +178,18 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   unsigned vm = 0u;
   static_assert(PER <= 32, "validity bits");
   if constexpr (SRC == kDense) {
-    const int32_t* row = a.scores + (int64_t)r * a.ld_scores;
+    // The visible scores as a buffer of nv * 4 bytes: the hardware returns 0
+    // for reads past it, so every lane loads with no branch or clamp, all
+    // loads are in flight at once, and the invisible ones are replaced after.
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.scores + (int64_t)r * a.ld_scores), (short)0, nv * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = i * BLOCK + tid;
-      sc[i] = e < nv ? __builtin_nontemporal_load(row + e) : INT32_MIN;
-      vm |= e < nv ? 1u << i : 0u;
+      const bool in = e < nv;
+      const int v = __builtin_amdgcn_raw_buffer_load_b32(row, e * 4, 0, 2);  // aux 2: non-temporal
+      sc[i] = in ? v : INT32_MIN;
+      vm |= in ? 1u << i : 0u;
     }
   } else if constexpr (SRC == kRecompute) {
     // S[t][j] = sum_h w[t][h] * max(0, <iq[t][h][:], ik[j][:]>), exact.
