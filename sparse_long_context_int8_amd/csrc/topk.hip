@@ -169,27 +169,36 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     return;
   }
 
-  // Elements of this token in registers, n_el of them; bit i of `vm` says
-  // whether register i holds one. Dense and recomputed elements are rows
-  // 0 .. nv-1 in order (element i*BLOCK + tid); candidates carry their row.
+  // Elements of this token in registers, n_el of them. Dense and recomputed
+  // elements are rows 0 .. nv-1 in order (element i*BLOCK + tid: register i
+  // holds one when tid < nv - i*BLOCK, a compare with a scalar); candidates
+  // carry their row, and bit i of `vm` says whether register i holds one.
   int sc[PER];
   int jx[SRC == kCandidate ? PER : 1];
   int n_el = nv;
   unsigned vm = 0u;
   static_assert(PER <= 32, "validity bits");
+  auto valid = [&](int i) -> bool {
+    if constexpr (SRC == kCandidate) return (vm >> i) & 1u;
+    else return tid < nv - i * BLOCK;
+  };
+  // Score range of the elements (dense rows: taken as they load).
+  int vmax = INT32_MIN, vmin = INT32_MAX;
   if constexpr (SRC == kDense) {
-    // The visible scores as a buffer of nv * 4 bytes: the hardware returns 0
-    // for reads past it, so every lane loads with no branch or clamp, all
-    // loads are in flight at once, and the invisible ones are replaced after.
+    // The visible scores as a buffer resource (one scalar base, one offset
+    // register per load). Every lane loads, past the visible rows the last
+    // visible score (nv >= 1 here), so no branch stands between the loads,
+    // all are in flight at once, and that copy changes neither the minimum
+    // nor the maximum; the element is then marked invisible (INT32_MIN).
     const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t*>(a.scores + (int64_t)r * a.ld_scores), (short)0, nv * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = i * BLOCK + tid;
-      const bool in = e < nv;
-      const int v = __builtin_amdgcn_raw_buffer_load_b32(row, e * 4, 0, 2);  // aux 2: non-temporal
-      sc[i] = in ? v : INT32_MIN;
-      vm |= in ? 1u << i : 0u;
+      const int v = __builtin_amdgcn_raw_buffer_load_b32(row, min(e, nv - 1) * 4, 0, 2);  // aux 2: non-temporal
+      vmax = max(vmax, v);
+      vmin = min(vmin, v);
+      sc[i] = valid(i) ? v : INT32_MIN;
     }
   } else if constexpr (SRC == kRecompute) {
     // S[t][j] = sum_h w[t][h] * max(0, <iq[t][h][:], ik[j][:]>), exact.
@@ -202,7 +211,6 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     for (int i = 0; i < PER; ++i) {
       const int e = i * BLOCK + tid;
       sc[i] = INT32_MIN;
-      vm |= e < nv ? 1u << i : 0u;
       if (e < nv) {
         const int4* krow = reinterpret_cast<const int4*>(f.ik + (int64_t)e * kIdxDim);
         int kv[16];
@@ -311,12 +319,13 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
       }
     }
   }
-  int vmax = INT32_MIN, vmin = INT32_MAX;
+  if constexpr (SRC != kDense) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if ((vm >> i) & 1u) {
-      vmax = max(vmax, sc[i]);
-      vmin = min(vmin, sc[i]);
+    for (int i = 0; i < PER; ++i) {
+      if (valid(i)) {
+        vmax = max(vmax, sc[i]);
+        vmin = min(vmin, sc[i]);
+      }
     }
   }
   vmax = wave_max_i(vmax);
@@ -356,7 +365,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if ((vm >> i) & 1u) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
+      if (valid(i)) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
     __syncthreads();
     find_bin<BLOCK>(hist, kBins1, k, &s_bin, &s_above, &s_count, red_c);
     const int bin1 = s_bin;
@@ -378,7 +387,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
         const int dbits = top - shift;  // digit width this pass (<= 8)
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-          if ((vm >> i) & 1u) {
+          if (valid(i)) {
             const u64 key = key_of(i);
             if ((key >> top) == prefix) atomicAdd(&hist[(key >> shift) & ((1u << dbits) - 1)], 1);
           }
@@ -416,7 +425,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if ((vm >> i) & 1u) {
+      if (valid(i)) {
         const u64 key = key_of(i);
         if (key >= thresh) atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
       }
@@ -433,7 +442,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
       for (int u = 0; u < G; ++u) {
         const int i = i0 + u;
         slot[u] = -1;
-        if ((vm >> i) & 1u) {
+        if (valid(i)) {
           const u64 key = key_of(i);
           if (key >= thresh) slot[u] = atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
         }
@@ -454,7 +463,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     const int jm = __builtin_amdgcn_readfirstlane(nv - 1 - (int)(thresh & emask));
     auto kept_of = [&](int i) -> bool {
       const bool pass = sc[i] > ts || (sc[i] == ts && (SRC == kCandidate ? jx[i] <= jm : tid <= jm - i * BLOCK));
-      return SRC == kCandidate ? (((vm >> i) & 1u) && pass) : pass;
+      return SRC == kCandidate ? (valid(i) && pass) : pass;
     };
     int mine = 0;
 #pragma unroll
