@@ -474,25 +474,36 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     int pos = mine_incl - mine;
 #pragma unroll
     for (int w = 0; w < NW; ++w) pos += w < wave ? red_a[w] : 0;
+    // The kept elements go out as scores and rows (two arrays over the
+    // collected space): the branch around the write is taken in nearly every
+    // register of every wave, so it holds as little as possible; keys and
+    // bucket counts are formed in passes over the collected elements, where
+    // every thread has work.
+    int* const kept_sc = reinterpret_cast<int*>(collected);
+    int* const kept_row = kept_sc + cap;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (kept_of(i)) {
         if (pos < cap) {  // by construction
-          const u64 key = key_of(i);
-          collected[pos] = key;
-          atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+          kept_sc[pos] = sc[i];
+          kept_row[pos] = SRC == kCandidate ? jx[i] : i * BLOCK + tid;
         }
         ++pos;
       }
     }
-    __syncthreads();
-    bucket_offsets<BLOCK>(hist, red_c);
     int total_kept = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) total_kept += red_a[w];
     total_kept = min(total_kept, cap);
+    auto kept_key = [&](int e) -> u64 {
+      return ((u64)((unsigned)kept_sc[e] - (unsigned)vmin) << ebits) | (u64)(unsigned)(nv - 1 - kept_row[e]);
+    };
+    __syncthreads();
+    for (int e = tid; e < total_kept; e += BLOCK) atomicAdd(&hist[(int)((kept_key(e) - thresh) >> shb)], 1);
+    __syncthreads();
+    bucket_offsets<BLOCK>(hist, red_c);
     for (int e = tid; e < total_kept; e += BLOCK) {
-      const u64 key = collected[e];
+      const u64 key = kept_key(e);
       bucketed[atomicAdd(&hist[(int)((key - thresh) >> shb)], 1)] = key;
     }
   }
