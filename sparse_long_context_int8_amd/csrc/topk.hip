@@ -70,17 +70,21 @@ __device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
 
 // Bins are scanned from the top. Finds the bin b in which the running count
 // of elements above first reaches `need`; returns it through shared slots.
-// `hist` holds nbins counters; all threads of the block must call this.
-template <int BLOCK>
+// `hist` holds nbins <= MAXBINS counters; all threads of the block must call
+// this. Thread t owns bins nbins-1 - (t*PER + i), i < PER, going down, and
+// keeps their counts in registers for the search.
+template <int BLOCK, int MAXBINS>
 __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, int* s_bin, int* s_above,
                                          int* s_count, int* red) {
+  constexpr int PER = (MAXBINS + BLOCK - 1) / BLOCK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (nbins + BLOCK - 1) / BLOCK;
-  // Thread t owns bins [nbins-1 - t*per, ...) going down.
+  int c[PER];
   int tot = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = nbins - 1 - (tid * per + i);
-    if (b >= 0) tot += hist[b];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = nbins - 1 - (tid * PER + i);
+    c[i] = b >= 0 ? hist[b] : 0;
+    tot += c[i];
   }
   const int incl = wave_incl_scan(tot, lane);
   if (lane == 63) red[wave] = incl;
@@ -89,18 +93,21 @@ __device__ __forceinline__ void find_bin(const int* hist, int nbins, int need, i
   for (int w = 0; w < wave; ++w) before += red[w];
   int above = before + incl - tot;
   if (above < need && need <= above + tot) {
-    for (int i = 0; i < per; ++i) {
-      const int b = nbins - 1 - (tid * per + i);
-      if (b < 0) break;
-      const int c = hist[b];
-      if (above < need && need <= above + c) {
-        *s_bin = b;
-        *s_above = above;
-        *s_count = c;
-        break;
+    // This thread's bins hold the need-th element: the first bin, going
+    // down, at which the running count reaches it (no more LDS reads).
+    int bin = -1, at = 0, cnt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (bin < 0 && need <= above + c[i]) {
+        bin = nbins - 1 - (tid * PER + i);
+        at = above;
+        cnt = c[i];
       }
-      above += c;
+      above += c[i];
     }
+    *s_bin = bin;
+    *s_above = at;
+    *s_count = cnt;
   }
   __syncthreads();
 }
@@ -112,9 +119,13 @@ template <int BLOCK>
 __device__ __forceinline__ void bucket_offsets(int* hist, int* red) {
   constexpr int kPer = kBins1 / BLOCK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c[kPer];
   int tot = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) tot += hist[kBins1 - 1 - (tid * kPer + i)];
+  for (int i = 0; i < kPer; ++i) {
+    c[i] = hist[kBins1 - 1 - (tid * kPer + i)];
+    tot += c[i];
+  }
   const int incl = wave_incl_scan(tot, lane);
   if (lane == 63) red[wave] = incl;
   __syncthreads();
@@ -122,10 +133,8 @@ __device__ __forceinline__ void bucket_offsets(int* hist, int* red) {
   for (int w = 0; w < wave; ++w) base += red[w];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int b = kBins1 - 1 - (tid * kPer + i);
-    const int c = hist[b];
-    hist[b] = base;
-    base += c;
+    hist[kBins1 - 1 - (tid * kPer + i)] = base;
+    base += c[i];
   }
   __syncthreads();
 }
@@ -367,7 +376,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     for (int i = 0; i < PER; ++i)
       if (valid(i)) atomicAdd(&hist[((unsigned)sc[i] - (unsigned)vmin) >> sh1], 1);
     __syncthreads();
-    find_bin<BLOCK>(hist, kBins1, k, &s_bin, &s_above, &s_count, red_c);
+    find_bin<BLOCK, kBins1>(hist, kBins1, k, &s_bin, &s_above, &s_count, red_c);
     const int bin1 = s_bin;
     int need = k - s_above;
     const int low_bits = sh1 + ebits;  // key bits below the coarse digit
@@ -393,7 +402,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
           }
         }
         __syncthreads();
-        find_bin<BLOCK>(hist, 1 << dbits, need, &s_bin, &s_above, &s_count, red_c);
+        find_bin<BLOCK, 256>(hist, 1 << dbits, need, &s_bin, &s_above, &s_count, red_c);
         need -= s_above;
         prefix = (prefix << dbits) | (u64)s_bin;
         top = shift;
