@@ -367,9 +367,14 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   // the refinement below only runs when that bin is crowded (heavy ties).
   const int cap = min(k + kSlack, BLOCK * PER);  // n_el <= BLOCK * PER
   u64 thresh = 0;
+  const int sh1 = sbits > kBits1 ? sbits - kBits1 : 0;
+  // With few registers per thread and a threshold on a coarse bin boundary,
+  // the coarse bins at or above it serve as the ordering buckets: hist
+  // already holds their counts, exactly the n_coarse kept elements.
+  bool coarse_buckets = false;
+  int n_coarse = 0;
   if (n_el > cap) {
     // 1. coarse pass on the top kBits1 bits of (score - min).
-    const int sh1 = sbits > kBits1 ? sbits - kBits1 : 0;
     for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
     __syncthreads();
 #pragma unroll
@@ -383,6 +388,8 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
     u64 prefix = (u64)bin1;            // key >> shift must equal this
     if (s_above + s_count <= cap || low_bits == 0) {
       thresh = prefix << low_bits;
+      coarse_buckets = PER <= kDirectPer && s_above + s_count <= cap;
+      n_coarse = s_above + s_count;
     } else {
       // 2. refine inside the bin with 8-bit digits of the remaining bits.
       int shift = ((low_bits + 7) / 8) * 8 - 8;
@@ -427,16 +434,24 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   const u64 kspan = key_hi - thresh;
   const int kbits = kspan ? 64 - __clzll(kspan) : 0;
   const int shb = kbits > kBits1 ? kbits - kBits1 : 0;
+  // key >> (ebits + sh1) is the coarse bin (score - min) >> sh1.
+  auto bucket_of = [&](u64 key) -> int {
+    return coarse_buckets ? (int)(key >> (ebits + sh1)) : (int)((key - thresh) >> shb);
+  };
   u64* const bucketed = keys;
-  __syncthreads();
-  for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
-  if constexpr (PER <= kDirectPer) {
+  if (!coarse_buckets) {
     __syncthreads();
+    for (int b = tid; b < kBins1; b += BLOCK) hist[b] = 0;
+  }
+  if constexpr (PER <= kDirectPer) {
+    if (!coarse_buckets) {
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (valid(i)) {
-        const u64 key = key_of(i);
-        if (key >= thresh) atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+      for (int i = 0; i < PER; ++i) {
+        if (valid(i)) {
+          const u64 key = key_of(i);
+          if (key >= thresh) atomicAdd(&hist[bucket_of(key)], 1);
+        }
       }
     }
     __syncthreads();
@@ -453,7 +468,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
         slot[u] = -1;
         if (valid(i)) {
           const u64 key = key_of(i);
-          if (key >= thresh) slot[u] = atomicAdd(&hist[(int)((key - thresh) >> shb)], 1);
+          if (key >= thresh) slot[u] = atomicAdd(&hist[bucket_of(key)], 1);
         }
       }
 #pragma unroll
@@ -518,8 +533,9 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   }
   __syncthreads();
   // After the scatter hist[b] is the end of bucket b; bucket 0 comes last, so
-  // hist[0] is the number of keys collected.
-  const int n_coll = min(hist[0], cap);
+  // hist[0] is the number of keys collected (with coarse buckets the bins
+  // below the threshold stay unfilled: their count is known).
+  const int n_coll = coarse_buckets ? n_coarse : min(hist[0], cap);
   // Ascending order (optional): the winners' rows are marked in a bitmap of
   // the visible rows (nv <= kMaxComp bits), which follows the bucketed keys
   // and their collected copy (the launcher reserves asc_bitmap_words(n_comp)
@@ -537,7 +553,7 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, const FusedArgs& f
   // it) is its start.
   for (int p = tid; p < n_coll; p += BLOCK) {
     const u64 key = bucketed[p];
-    const int b = (int)((key - thresh) >> shb);
+    const int b = bucket_of(key);
     const int st = b + 1 < kBins1 ? hist[b + 1] : 0, en = hist[b];
     int place = st;
     // Four bucket entries per step (independent reads; most buckets hold
