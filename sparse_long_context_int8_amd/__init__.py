@@ -154,10 +154,9 @@ def _validate(t, dtype=None, name="tensor", numel=0):
         raise ValueError(f"{name} holds {t.numel()} elements, the descriptor needs {numel}")
 
 
-def _ptr(t, dtype=None, name="tensor", numel=0):
-    """Device pointer of a contiguous device tensor (None -> NULL; an int is
-    a raw address, used by tests of the C checks)."""
-    _validate(t, dtype, name, numel)
+def _addr(t, name):
+    """Device pointer of an argument _validate has accepted (None -> NULL; an
+    int is a raw address, used by tests of the C checks)."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -167,29 +166,40 @@ def _ptr(t, dtype=None, name="tensor", numel=0):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _ptr(t, dtype=None, name="tensor", numel=0):
+    """Device pointer of a contiguous device tensor, validated."""
+    _validate(t, dtype, name, numel)
+    return _addr(t, name)
+
+
 def _ptrs(*specs):
     """Pointers of several arguments, each (tensor, dtype, name, numel):
     every argument is validated before any is looked up on the device."""
     for spec in specs:
         _validate(*spec)
-    return [_ptr(*spec) for spec in specs]
+    return [_addr(spec[0], spec[2]) for spec in specs]
+
+
+# Element count of each argument as include/spmla.h lays it out, from the
+# descriptor fields it needs (each field read of a ctypes structure costs
+# host time on every call).
+_COUNTS = {
+    "q": lambda d: d.n_q * d.n_heads * d.d_qk,
+    "kv_comp": lambda d: d.n_comp * d.d_qk,
+    "kv_raw": lambda d: d.n_raw * d.d_qk,
+    "iq": lambda d: d.n_q * d.idx_heads * d.idx_dim,
+    "iw": lambda d: d.n_q * d.idx_heads,
+    "ik": lambda d: d.n_comp * d.idx_dim,
+    "scores": lambda d: d.n_q * d.n_comp,
+    "sel": lambda d: d.n_q * d.top_k,
+    "out": lambda d: d.n_q * d.n_heads * d.d_v,
+    "lse": lambda d: d.n_q * d.n_heads,
+}
 
 
 def _n(desc, name: str) -> int:
     """Element count of an argument as include/spmla.h lays it out."""
-    n_q, n_comp = desc.n_q, desc.n_comp
-    return {
-        "q": n_q * desc.n_heads * desc.d_qk,
-        "kv_comp": n_comp * desc.d_qk,
-        "kv_raw": desc.n_raw * desc.d_qk,
-        "iq": n_q * desc.idx_heads * desc.idx_dim,
-        "iw": n_q * desc.idx_heads,
-        "ik": n_comp * desc.idx_dim,
-        "scores": n_q * n_comp,
-        "sel": n_q * desc.top_k,
-        "out": n_q * desc.n_heads * desc.d_v,
-        "lse": n_q * desc.n_heads,
-    }[name]
+    return _COUNTS[name](desc)
 
 
 def _attn_ptrs(desc, q, kv_comp, kv_raw, sel, out, lse):
