@@ -312,8 +312,10 @@ def prepare_prefill(sp, torch, workloads, w):
 
 
 def time_steps(torch, w, prep, steps, warmup):
-    """`warmup` untimed spmla_prefill steps, then `steps` timed ones: HIP
-    events on the launch stream around each step.
+    """`warmup` untimed spmla_prefill steps, then `steps` timed ones between
+    two HIP events on the launch stream (an event after every step would
+    cost the GPU a few microseconds between steps, a sizeable share of a
+    decode step).
 
     The GPU leaves its sustained clocks within a few milliseconds of idling
     and needs some 25-30 ms of work to return to them, so nothing on the host
@@ -321,29 +323,26 @@ def time_steps(torch, w, prep, steps, warmup):
     steps: the events are made first, and their times are read afterwards
     (step_times)."""
     step = prep["step"]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     log(f"{w.name}: warmup {warmup}, then {steps} timed steps")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record()
-    for i in range(steps):
+    for _ in range(steps):
         step()
-        evs[i + 1].record()
+    evs[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return {"evs": evs, "wall": wall}
+    return {"evs": evs, "steps": steps, "wall": wall}
 
 
 def step_times(w, timed):
-    """Per-step and mean times of a time_steps run, and its throughput."""
-    evs = timed["evs"]
-    steps = len(evs) - 1
-    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    total_ms = evs[0].elapsed_time(evs[-1])
-    return {"per_step": per_step, "wall": timed["wall"], "ms_per_step": total_ms / steps,
-            "value": w.n_q * steps / (total_ms / 1e3)}
+    """Mean step time of a time_steps run, and its throughput."""
+    evs, steps = timed["evs"], timed["steps"]
+    total_ms = evs[0].elapsed_time(evs[1])
+    return {"wall": timed["wall"], "ms_per_step": total_ms / steps, "value": w.n_q * steps / (total_ms / 1e3)}
 
 
 def main():
@@ -491,7 +490,7 @@ def main():
     t_ceil = t_ceil_by_nbuf[best_nbuf]
 
     t.update(step_times(w, timed))
-    per_step, wall, ms_per_step, value = t["per_step"], t["wall"], t["ms_per_step"], t["value"]
+    wall, ms_per_step, value = t["wall"], t["ms_per_step"], t["value"]
 
     bytes_q = attn_bytes_per_query(w)
     flops_q = attn_flops_per_query(w)
@@ -554,8 +553,6 @@ def main():
             "d_v": w.d_v,
             "indexer": "int8 4x64",
         },
-        "step_ms_median": round(float(np.median(per_step)), 4),
-        "step_ms_min": round(float(np.min(per_step)), 4),
         "wall_s": round(wall, 3),
         # The step-wise ABI calls per band (indexer_scores writes the full
         # score band; spmla_prefill may select without it; sparse_attn is the
@@ -582,7 +579,6 @@ def main():
             res["workloads"][name] = {
                 "n_q": we.n_q, "q_pos0": we.q_pos0, "top_k": we.top_k, "bands": sp.spmla_num_bands(te["desc"]),
                 "ms_per_step": round(te["ms_per_step"], 4),
-                "step_ms_median": round(float(np.median(te["per_step"])), 4),
                 "tokens_per_s": round(te["value"], 1),
                 "step_roofline": step_roofline(we, te["ms_per_step"]),
             }
